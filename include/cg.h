@@ -1,0 +1,191 @@
+/*
+ * cg.h -- C ABI of the MI355X (gfx950) CacheGen-style KV-cache codec.
+ *
+ * The codec compresses an fp16 K/V cache in three steps that the pages
+ * describe ("CacheGen实战：KV缓存压缩与流式传输在大型语言模型服务中的高效应用",
+ * section 1): quantize with one step per layer group (fine in shallow layers,
+ * coarse in deep ones), store token-to-token differences, and entropy-code
+ * the differences group by group. The context is cut into chunks (section
+ * 2.1: 1.5K tokens) that are encoded, shipped and decoded independently, and
+ * the receiver decodes on the GPU straight into the model's cache (section
+ * 2.3), which may be paged ("vLLM中的PagedAttention优化" in the KV-cache
+ * optimisation article: physical blocks found through a block table).
+ *
+ * Bit-level definition (the pages leave it open; these are the readings):
+ *   q      = clamp(round_half_even(fl32(x / step[group(layer)])), -32768, 32767), NaN -> 0
+ *   d_0    = q[first token of the chunk] (raw);  d_i = wrap16(q_i - q_{i-1})
+ *   symbol = d_i + 127 if |d_i| <= 127, else 255 (escape) + raw u16(d_i)
+ *   tables = per (layer group, K|V, head, dim) symbol counts, normalised to
+ *            12-bit frequencies (sum 4096)
+ *   coder  = static rANS, 32-bit state in [2^16, 2^32), 16-bit words; a group
+ *            = (chunk, layer, K|V, head, 64-dim slice), lane k codes dim
+ *            64*slice + k, 64 lanes interleaved word by word
+ *   x_hat  = fp16_round_half_even(fl32(float(q) * step))
+ *
+ * Layouts (all little-endian, element = fp16 bits as uint16_t):
+ *   KV tensor  x[layer][2 (K,V)][kv_head][token][head_dim]
+ *   paged pool pool[layer][2][num_blocks][kv_head][16][head_dim]
+ *   tables blob, chunk record: see cg_tables_format_bytes / cg_encode.
+ *
+ * Conventions for every call:
+ *   - Pointers named *_dev are device pointers the CALLER allocates and owns;
+ *     the library allocates no device memory and keeps no state between calls.
+ *   - Calls are asynchronous and ordered on `stream`. The return value only
+ *     reports argument checks and launch failures (CG_ERR_INVALID_ARG,
+ *     CG_ERR_UNSUPPORTED, CG_ERR_HIP). Errors that depend on data are written
+ *     to the device word *status_dev (0 = OK, else a CG_ERR_* code); the call
+ *     first resets it to 0. Read it after synchronising the stream.
+ *   - Alignment: tables, workspaces, containers and refs must be 256-byte
+ *     aligned; x / y / pool must be 2-byte aligned.
+ *   - Two calls that share an output or workspace buffer and overlap in time
+ *     race; ordering on one stream is enough.
+ */
+#ifndef CG_H_
+#define CG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t cg_status;
+#define CG_OK 0
+#define CG_ERR_INVALID_ARG (-1) /* bad argument, shape, pointer or block-table entry */
+#define CG_ERR_UNSUPPORTED (-2) /* valid but outside this build's limits             */
+#define CG_ERR_CAPACITY (-3)    /* output buffer too small (encode)                  */
+#define CG_ERR_HIP (-4)         /* a HIP launch or runtime call failed                */
+#define CG_ERR_CORRUPT (-5)     /* a record or stream failed its integrity checks      */
+#define CG_ERR_TABLE (-6)       /* a symbol to encode has frequency 0 in the table     */
+
+/* Shape of one KV cache. head_dim must be a multiple of 64. Limits:
+ * layers <= 1024, layers*tokens < 2^32, chunk_tokens <= 1<<20. */
+typedef struct cg_shape {
+  int32_t layers;       /* L */
+  int32_t kv_heads;     /* H */
+  int32_t head_dim;     /* D */
+  int32_t chunk_tokens; /* C: delta-reset and record unit ("CacheGen实战" 2.1: 1536) */
+  int64_t tokens;       /* T */
+} cg_shape;
+
+/* One quality level ("CacheGen实战" 3.1: high 0.3/0.8/1.2, balanced
+ * 0.5/1.0/1.5, fast 0.8/1.5/2.0). Host pointers. */
+typedef struct cg_level {
+  int32_t level_id;           /* stored in tables and records, 0..65535        */
+  int32_t n_groups;           /* G, 1..255                                      */
+  const uint8_t* layer_group; /* [layers], each < n_groups                      */
+  const float* step;          /* [n_groups], finite and > 0                      */
+} cg_level;
+
+/* Where one chunk record lives, for the decoders. Device array. */
+typedef struct cg_chunk_ref {
+  const uint8_t* record; /* device pointer to a record written by cg_encode, 256-B aligned */
+  uint64_t bytes;        /* readable bytes at `record` (>= the record's size)               */
+  int32_t table;         /* index into the decoder's levels / tables arrays                 */
+  int32_t reserved;      /* 0                                                             */
+} cg_chunk_ref;
+
+/* Library version (1) and a readable name for a status code. */
+int32_t cg_version(void);
+const char* cg_status_string(cg_status s);
+
+/* ---- frequency tables -------------------------------------------------- */
+
+/* Bytes of a tables blob for `n_groups` layer groups (format section plus the
+ * decoder/encoder lookup section that follows it), or 0 for a bad shape. */
+size_t cg_tables_bytes(const cg_shape* shape, int32_t n_groups);
+
+/* Bytes of the format section alone: the part a file or another
+ * implementation must reproduce. Layout: 64-byte header ("CGTB", version,
+ * layers, kv_heads, head_dim, n_groups, level_id, chunk_tokens, tokens u64,
+ * f_offset, 0, format_bytes u64, 0 u64), f32 step[G], u8 layer_group[L], zero
+ * pad to f_offset (256-aligned), u16 f[G][2][H][D][256]. */
+size_t cg_tables_format_bytes(const cg_shape* shape, int32_t n_groups);
+
+/* Workspace of cg_build_tables (symbol counts), or 0 for a bad shape. */
+size_t cg_build_workspace_bytes(const cg_shape* shape, int32_t n_groups);
+
+/* Per-channel statistics ("CacheGen：…技术解析", 「量化编码器设计」: statistics
+ * per channel, entropy coding of the integer indices; "CacheGen实战"
+ * section 1: grouped entropy coding). Counts the symbols of tokens 1..n-1 of
+ * every chunk of x_dev per (layer group, K|V, head, dim), normalises each
+ * table to 12 bits and writes the blob to tables_dev (cg_tables_bytes).
+ * stats_dev (optional, u64[4]) receives {elements, saturated, nan, escapes}.
+ * Data errors: none. */
+cg_status cg_build_tables(const cg_shape* shape, const cg_level* level, const uint16_t* x_dev,
+                          void* tables_dev, void* ws_dev, size_t ws_bytes, uint64_t* stats_dev,
+                          hipStream_t stream);
+
+/* ---- encode -------------------------------------------------------------- */
+
+/* Worst-case bytes of the records of chunks [chunk_begin, chunk_end). */
+size_t cg_encode_bound(const cg_shape* shape, int64_t chunk_begin, int64_t chunk_end);
+
+/* Workspace of cg_encode for that chunk range, or 0 for a bad range. */
+size_t cg_encode_workspace_bytes(const cg_shape* shape, int64_t chunk_begin, int64_t chunk_end);
+
+/* Encodes chunks [chunk_begin, chunk_end) of x_dev with the tables of one
+ * level ("CacheGen实战" 2.1: every chunk is pre-encoded per quality level).
+ * Writes the chunk records back to back to out_dev and their byte offsets to
+ * chunk_offsets_dev[0 .. n] (u64, offsets[n] = total). A record is: 64-byte
+ * header ("CGCK", version, chunk_index, level_id, token_start u64, n_tokens,
+ * n_groups, layers, kv_heads, head_dim, data_start, record_bytes u64,
+ * data_bytes u64), u64 group_offset[n_groups+1] (from the data start,
+ * multiples of 16), u32 group_words[n_groups], zero pad to data_start
+ * (256-aligned), the group word streams in (layer, K|V, head, slice) order
+ * each zero-padded to 16 bytes, zero pad to record_bytes (256-aligned).
+ * Data errors: CG_ERR_CAPACITY (total > out_cap; offsets still hold the
+ * needed sizes, out_dev is not written), CG_ERR_TABLE, CG_ERR_INVALID_ARG
+ * (tables blob does not match the shape). */
+cg_status cg_encode(const cg_shape* shape, const cg_level* level, const void* tables_dev,
+                    const uint16_t* x_dev,
+                    int64_t chunk_begin, int64_t chunk_end, uint8_t* out_dev, uint64_t out_cap,
+                    uint64_t* chunk_offsets_dev, void* ws_dev, size_t ws_bytes,
+                    int32_t* status_dev, hipStream_t stream);
+
+/* Fills refs_dev[i] = {base_dev + offsets_dev[i], offsets_dev[i+1] - offsets_dev[i],
+ * table, 0} for i < n (a helper to decode what cg_encode wrote). */
+cg_status cg_make_refs(const uint8_t* base_dev, const uint64_t* offsets_dev, int32_t n,
+                       int32_t table, cg_chunk_ref* refs_dev, hipStream_t stream);
+
+/* ---- decode -------------------------------------------------------------- */
+
+/* Decodes the records named by refs_dev[0 .. n_refs) into the contiguous
+ * tensor y_dev ("CacheGen实战" 2.3: parallel GPU decode). Record i is read
+ * with tables_dev[refs[i].table], which must have been built for
+ * levels[refs[i].table]; records of different levels may be mixed (section
+ * 2.1). Only the token ranges of the given chunks are written.
+ * n_levels <= 8. levels and tables_dev are host arrays; tables_dev[k] is a
+ * device pointer. Data errors: CG_ERR_CORRUPT (bad record header, group
+ * offsets, final rANS state or word count), CG_ERR_INVALID_ARG (table index
+ * out of range, blob not matching its level). */
+cg_status cg_decode(const cg_shape* shape, int32_t n_levels, const cg_level* levels,
+                    const void* const* tables_dev, const cg_chunk_ref* refs_dev, int32_t n_refs,
+                    uint16_t* y_dev, int32_t* status_dev, hipStream_t stream);
+
+/* As cg_decode, but the destination is a paged cache: token t of layer l,
+ * K|V kv, head h goes to pool_dev[l][kv][block_table_dev[t/16]][h][t%16][:]
+ * ("vLLM中的PagedAttention优化": non-contiguous physical blocks). The block
+ * table is indexed by absolute token block, int32 [ceil(tokens/16)]. Pool
+ * entries of other blocks are not touched. Data errors: as cg_decode, plus
+ * CG_ERR_INVALID_ARG when an entry used by a chunk is outside
+ * [0, num_blocks) (that chunk is then not written). */
+cg_status cg_decode_paged(const cg_shape* shape, int32_t n_levels, const cg_level* levels,
+                          const void* const* tables_dev, const cg_chunk_ref* refs_dev,
+                          int32_t n_refs, uint16_t* pool_dev, int64_t num_blocks,
+                          const int32_t* block_table_dev, int32_t* status_dev,
+                          hipStream_t stream);
+
+/* ---- measurement helper ---------------------------------------------------- */
+
+/* Plain device copy of `bytes` (a multiple of 16) with the library's launch
+ * style; used to calibrate achievable bandwidth and HBM counters. */
+cg_status cg_copy(void* dst_dev, const void* src_dev, uint64_t bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CG_H_ */

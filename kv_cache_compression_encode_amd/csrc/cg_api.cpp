@@ -1,0 +1,356 @@
+// cg_api.cpp -- C ABI of the gfx950 KV-cache codec: argument checks, buffer
+// sizing, workspace carving and kernel launches. No device memory is
+// allocated here; every buffer comes from the caller.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "cg_layout.h"
+
+using namespace cg;
+
+namespace {
+
+// Shapes the kernels' index arithmetic and grids are sized for.
+cg_status check_shape(const cg_shape* sp, Shape* out) {
+  if (!sp) return CG_ERR_INVALID_ARG;
+  const cg_shape& s = *sp;
+  if (s.layers < 1 || s.kv_heads < 1 || s.head_dim < 1 || s.chunk_tokens < 1 || s.tokens < 1)
+    return CG_ERR_INVALID_ARG;
+  if (s.head_dim % 64 != 0) return CG_ERR_UNSUPPORTED;
+  if (s.layers > kMaxLayers || s.chunk_tokens > (1 << 20) || s.kv_heads > (1 << 16) ||
+      s.head_dim > (1 << 16))
+    return CG_ERR_UNSUPPORTED;
+  if ((uint64_t)s.layers * (uint64_t)s.tokens >= (1ull << 32)) return CG_ERR_UNSUPPORTED;
+  const uint64_t gpc = (uint64_t)s.layers * 2 * s.kv_heads * (s.head_dim / 64);
+  if (gpc >= (1ull << 31)) return CG_ERR_UNSUPPORTED;
+  if (out) {
+    out->L = s.layers;
+    out->H = s.kv_heads;
+    out->D = s.head_dim;
+    out->C = s.chunk_tokens;
+    out->S = s.head_dim / 64;
+    out->T = s.tokens;
+  }
+  return CG_OK;
+}
+
+cg_status check_level(const cg_level* lv, const Shape& s) {
+  if (!lv || !lv->layer_group || !lv->step) return CG_ERR_INVALID_ARG;
+  if (lv->n_groups < 1 || lv->n_groups > kMaxGroups) return CG_ERR_INVALID_ARG;
+  if (lv->level_id < 0 || lv->level_id > 65535) return CG_ERR_INVALID_ARG;
+  for (int l = 0; l < s.L; ++l)
+    if (lv->layer_group[l] >= lv->n_groups) return CG_ERR_INVALID_ARG;
+  for (int g = 0; g < lv->n_groups; ++g)
+    if (!(lv->step[g] > 0.0f) || !std::isfinite(lv->step[g])) return CG_ERR_INVALID_ARG;
+  return CG_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+cg_status hip_status(hipError_t e) { return e == hipSuccess ? CG_OK : CG_ERR_HIP; }
+
+struct EncodeWs {
+  uint64_t gw, gs, go, rb, scratch, total;
+};
+
+EncodeWs encode_ws_layout(const Shape& s, int64_t n_ch, uint64_t cap_words) {
+  const uint64_t gpc = (uint64_t)groups_per_chunk(s.L, s.H, s.D);
+  EncodeWs w;
+  uint64_t o = 0;
+  w.gw = o;
+  o = align_up(o + 4 * gpc * n_ch, 256);
+  w.gs = o;
+  o = align_up(o + 4 * gpc * n_ch, 256);
+  w.go = o;
+  o = align_up(o + 8 * (gpc + 1) * n_ch, 256);
+  w.rb = o;
+  o = align_up(o + 8 * (uint64_t)n_ch, 256);
+  w.scratch = o;
+  o = align_up(o + 2 * cap_words * gpc * n_ch, 256);
+  w.total = o;
+  return w;
+}
+
+cg_status check_range(const Shape& s, int64_t cb, int64_t ce) {
+  const int64_t nch = n_chunks(s.T, s.C);
+  if (cb < 0 || ce <= cb || ce > nch) return CG_ERR_INVALID_ARG;
+  return CG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t cg_version(void) { return 1; }
+
+const char* cg_status_string(cg_status st) {
+  switch (st) {
+    case CG_OK: return "ok";
+    case CG_ERR_INVALID_ARG: return "invalid argument";
+    case CG_ERR_UNSUPPORTED: return "unsupported shape or size";
+    case CG_ERR_CAPACITY: return "output buffer too small";
+    case CG_ERR_HIP: return "HIP launch or runtime error";
+    case CG_ERR_CORRUPT: return "corrupt record or stream";
+    case CG_ERR_TABLE: return "symbol missing from frequency table";
+    default: return "unknown status";
+  }
+}
+
+size_t cg_tables_bytes(const cg_shape* shape, int32_t n_groups) {
+  Shape s;
+  if (check_shape(shape, &s) != CG_OK || n_groups < 1 || n_groups > kMaxGroups) return 0;
+  return (size_t)tb_total_bytes(s.L, s.H, s.D, n_groups);
+}
+
+size_t cg_tables_format_bytes(const cg_shape* shape, int32_t n_groups) {
+  Shape s;
+  if (check_shape(shape, &s) != CG_OK || n_groups < 1 || n_groups > kMaxGroups) return 0;
+  return (size_t)tb_format_bytes(s.L, s.H, s.D, n_groups);
+}
+
+size_t cg_build_workspace_bytes(const cg_shape* shape, int32_t n_groups) {
+  Shape s;
+  if (check_shape(shape, &s) != CG_OK || n_groups < 1 || n_groups > kMaxGroups) return 0;
+  return (size_t)align_up(tb_n_tables(n_groups, s.H, s.D) * 256 * 4, 256);
+}
+
+cg_status cg_build_tables(const cg_shape* shape, const cg_level* level, const uint16_t* x_dev,
+                          void* tables_dev, void* ws_dev, size_t ws_bytes, uint64_t* stats_dev,
+                          hipStream_t stream) {
+  Shape s;
+  cg_status rc = check_shape(shape, &s);
+  if (rc != CG_OK) return rc;
+  if ((rc = check_level(level, s)) != CG_OK) return rc;
+  if (!x_dev || !tables_dev || !ws_dev || !aligned(x_dev, 2) || !aligned(tables_dev, 256) ||
+      !aligned(ws_dev, 256) || (stats_dev && !aligned(stats_dev, 8)))
+    return CG_ERR_INVALID_ARG;
+  const int G = level->n_groups;
+  if (ws_bytes < cg_build_workspace_bytes(shape, G)) return CG_ERR_INVALID_ARG;
+  const uint64_t ntab = tb_n_tables(G, s.H, s.D);
+  if ((uint64_t)s.L * 2 * s.H * s.S >= (1ull << 31) || ntab / 4 + 1 >= (1ull << 31))
+    return CG_ERR_UNSUPPORTED;
+
+  uint32_t* counts = static_cast<uint32_t*>(ws_dev);
+  uint8_t* blob = static_cast<uint8_t*>(tables_dev);
+  hipError_t e = launch_fill_u32(counts, 0, ntab * 256, stream);
+  if (e == hipSuccess && stats_dev)
+    e = launch_fill_u32(reinterpret_cast<uint32_t*>(stats_dev), 0, 8, stream);
+  if (e != hipSuccess) return CG_ERR_HIP;
+
+  BlobInitArgs bi;
+  std::memset(&bi, 0, sizeof(bi));
+  bi.blob = blob;
+  bi.L = s.L;
+  bi.H = s.H;
+  bi.D = s.D;
+  bi.G = G;
+  bi.C = s.C;
+  bi.level_id = level->level_id;
+  bi.T = s.T;
+  for (int g = 0; g < G; ++g) bi.step[g] = level->step[g];
+  for (int l = 0; l < s.L; ++l) bi.lg[l] = level->layer_group[l];
+  if ((e = launch_blob_init(bi, stream)) != hipSuccess) return CG_ERR_HIP;
+
+  QCheckArgs qa;
+  qa.blob = blob;
+  qa.qflags = reinterpret_cast<uint32_t*>(blob + tb_qflag_offset(s.L, s.H, s.D, G));
+  qa.L = s.L;
+  qa.G = G;
+  if ((e = launch_qcheck(qa, stream)) != hipSuccess) return CG_ERR_HIP;
+
+  HistArgs ha;
+  ha.s = s;
+  ha.x = x_dev;
+  ha.blob = blob;
+  ha.counts = counts;
+  ha.stats = reinterpret_cast<unsigned long long*>(stats_dev);
+  ha.G = G;
+  if ((e = launch_hist(ha, stream)) != hipSuccess) return CG_ERR_HIP;
+
+  NormArgs na;
+  na.counts = counts;
+  na.blob = blob;
+  na.f_off = tb_f_offset(s.L, G);
+  na.enc_off = tb_enc_offset(s.L, s.H, s.D, G);
+  na.dec_off = tb_dec_offset(s.L, s.H, s.D, G);
+  na.n_tables = (int64_t)ntab;
+  return hip_status(launch_norm(na, stream));
+}
+
+size_t cg_encode_bound(const cg_shape* shape, int64_t chunk_begin, int64_t chunk_end) {
+  Shape s;
+  if (check_shape(shape, &s) != CG_OK || check_range(s, chunk_begin, chunk_end) != CG_OK) return 0;
+  const int64_t gpc = groups_per_chunk(s.L, s.H, s.D);
+  uint64_t total = 0;
+  for (int64_t c = chunk_begin; c < chunk_end; ++c) {
+    const uint64_t g = align_up(2 * group_cap_words(chunk_len(s.T, s.C, c)), 16);
+    total += align_up(rec_data_start(gpc) + g * (uint64_t)gpc, 256);
+  }
+  return (size_t)total;
+}
+
+size_t cg_encode_workspace_bytes(const cg_shape* shape, int64_t chunk_begin, int64_t chunk_end) {
+  Shape s;
+  if (check_shape(shape, &s) != CG_OK || check_range(s, chunk_begin, chunk_end) != CG_OK) return 0;
+  const uint64_t cap = group_cap_words(chunk_len(s.T, s.C, chunk_begin));
+  return (size_t)encode_ws_layout(s, chunk_end - chunk_begin, cap).total;
+}
+
+cg_status cg_encode(const cg_shape* shape, const cg_level* level, const void* tables_dev,
+                    const uint16_t* x_dev, int64_t chunk_begin, int64_t chunk_end,
+                    uint8_t* out_dev, uint64_t out_cap, uint64_t* chunk_offsets_dev, void* ws_dev,
+                    size_t ws_bytes, int32_t* status_dev, hipStream_t stream) {
+  Shape s;
+  cg_status rc = check_shape(shape, &s);
+  if (rc != CG_OK) return rc;
+  if ((rc = check_level(level, s)) != CG_OK) return rc;
+  if ((rc = check_range(s, chunk_begin, chunk_end)) != CG_OK) return rc;
+  if (!tables_dev || !x_dev || !out_dev || !chunk_offsets_dev || !ws_dev || !status_dev ||
+      !aligned(tables_dev, 256) || !aligned(x_dev, 2) || !aligned(out_dev, 256) ||
+      !aligned(chunk_offsets_dev, 8) || !aligned(ws_dev, 256) || !aligned(status_dev, 4))
+    return CG_ERR_INVALID_ARG;
+  const int64_t n = chunk_end - chunk_begin;
+  const uint64_t cap = group_cap_words(chunk_len(s.T, s.C, chunk_begin));
+  const EncodeWs w = encode_ws_layout(s, n, cap);
+  if (ws_bytes < w.total) return CG_ERR_INVALID_ARG;
+  const int G = level->n_groups;
+  const int64_t gpc = groups_per_chunk(s.L, s.H, s.D);
+  if ((uint64_t)n * G * 2 * s.H * s.S >= (1ull << 31) || cap >= (1ull << 32)) return CG_ERR_UNSUPPORTED;
+  const int gpb = 16;  // groups per copy block
+  if ((uint64_t)n * (1 + (gpc + gpb - 1) / gpb) >= (1ull << 31)) return CG_ERR_UNSUPPORTED;
+
+  uint8_t* ws = static_cast<uint8_t*>(ws_dev);
+  hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(status_dev), 0, 1, stream);
+  if (e != hipSuccess) return CG_ERR_HIP;
+
+  EncodeArgs ea;
+  ea.s = s;
+  ea.x = x_dev;
+  ea.blob = static_cast<const uint8_t*>(tables_dev);
+  ea.G = G;
+  ea.chunk_begin = chunk_begin;
+  ea.n_chunks = n;
+  ea.cap_words = cap;
+  ea.scratch = reinterpret_cast<uint16_t*>(ws + w.scratch);
+  ea.group_words = reinterpret_cast<uint32_t*>(ws + w.gw);
+  ea.group_start = reinterpret_cast<uint32_t*>(ws + w.gs);
+  ea.status = status_dev;
+  if ((e = launch_encode(ea, stream)) != hipSuccess) return CG_ERR_HIP;
+
+  LayoutArgs la;
+  la.gpc = gpc;
+  la.n_chunks = n;
+  la.group_words = ea.group_words;
+  la.group_off = reinterpret_cast<uint64_t*>(ws + w.go);
+  la.rec_bytes = reinterpret_cast<uint64_t*>(ws + w.rb);
+  if ((e = launch_layout(la, stream)) != hipSuccess) return CG_ERR_HIP;
+
+  ChunkScanArgs ca;
+  ca.n_chunks = n;
+  ca.rec_bytes = la.rec_bytes;
+  ca.chunk_offsets = chunk_offsets_dev;
+  ca.out_cap = out_cap;
+  ca.status = status_dev;
+  if ((e = launch_chunk_scan(ca, stream)) != hipSuccess) return CG_ERR_HIP;
+
+  WriteArgs wa;
+  wa.s = s;
+  wa.gpc = gpc;
+  wa.chunk_begin = chunk_begin;
+  wa.n_chunks = n;
+  wa.blob = ea.blob;
+  wa.cap_words = cap;
+  wa.scratch = ea.scratch;
+  wa.group_words = ea.group_words;
+  wa.group_start = ea.group_start;
+  wa.group_off = la.group_off;
+  wa.rec_bytes = la.rec_bytes;
+  wa.chunk_offsets = chunk_offsets_dev;
+  wa.out = out_dev;
+  wa.out_cap = out_cap;
+  wa.groups_per_block = gpb;
+  return hip_status(launch_write(wa, stream));
+}
+
+cg_status cg_make_refs(const uint8_t* base_dev, const uint64_t* offsets_dev, int32_t n,
+                       int32_t table, cg_chunk_ref* refs_dev, hipStream_t stream) {
+  if (!base_dev || !offsets_dev || !refs_dev || n < 1 || table < 0 || table >= kMaxLevels ||
+      !aligned(offsets_dev, 8) || !aligned(refs_dev, 8))
+    return CG_ERR_INVALID_ARG;
+  return hip_status(launch_make_refs(base_dev, offsets_dev, n, table, refs_dev, stream));
+}
+
+static cg_status decode_common(const cg_shape* shape, int32_t n_levels, const cg_level* levels,
+                               const void* const* tables_dev, const cg_chunk_ref* refs_dev,
+                               int32_t n_refs, int32_t* status_dev, DecodeArgs* a) {
+  Shape s;
+  cg_status rc = check_shape(shape, &s);
+  if (rc != CG_OK) return rc;
+  if (n_levels < 1 || n_levels > kMaxLevels || !levels || !tables_dev || !refs_dev || n_refs < 1 ||
+      !status_dev || !aligned(refs_dev, 8) || !aligned(status_dev, 4))
+    return CG_ERR_INVALID_ARG;
+  std::memset(a, 0, sizeof(*a));
+  int g_max = 0;
+  for (int k = 0; k < n_levels; ++k) {
+    if ((rc = check_level(&levels[k], s)) != CG_OK) return rc;
+    if (!tables_dev[k] || !aligned(tables_dev[k], 256)) return CG_ERR_INVALID_ARG;
+    for (int k2 = 0; k2 < k; ++k2)
+      if (levels[k2].level_id == levels[k].level_id && tables_dev[k2] != tables_dev[k])
+        return CG_ERR_INVALID_ARG;
+    a->tables[k] = static_cast<const uint8_t*>(tables_dev[k]);
+    a->level_id[k] = levels[k].level_id;
+    a->n_groups[k] = levels[k].n_groups;
+    if (levels[k].n_groups > g_max) g_max = levels[k].n_groups;
+  }
+  if ((uint64_t)n_refs * g_max * 2 * s.H * s.S >= (1ull << 31)) return CG_ERR_UNSUPPORTED;
+  a->s = s;
+  a->refs = refs_dev;
+  a->n_refs = n_refs;
+  a->n_tables = n_levels;
+  a->g_max = g_max;
+  a->status = status_dev;
+  return CG_OK;
+}
+
+cg_status cg_decode(const cg_shape* shape, int32_t n_levels, const cg_level* levels,
+                    const void* const* tables_dev, const cg_chunk_ref* refs_dev, int32_t n_refs,
+                    uint16_t* y_dev, int32_t* status_dev, hipStream_t stream) {
+  DecodeArgs a;
+  cg_status rc = decode_common(shape, n_levels, levels, tables_dev, refs_dev, n_refs, status_dev, &a);
+  if (rc != CG_OK) return rc;
+  if (!y_dev || !aligned(y_dev, 2)) return CG_ERR_INVALID_ARG;
+  a.y = y_dev;
+  hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(status_dev), 0, 1, stream);
+  if (e != hipSuccess) return CG_ERR_HIP;
+  return hip_status(launch_decode(a, false, stream));
+}
+
+cg_status cg_decode_paged(const cg_shape* shape, int32_t n_levels, const cg_level* levels,
+                          const void* const* tables_dev, const cg_chunk_ref* refs_dev,
+                          int32_t n_refs, uint16_t* pool_dev, int64_t num_blocks,
+                          const int32_t* block_table_dev, int32_t* status_dev,
+                          hipStream_t stream) {
+  DecodeArgs a;
+  cg_status rc = decode_common(shape, n_levels, levels, tables_dev, refs_dev, n_refs, status_dev, &a);
+  if (rc != CG_OK) return rc;
+  if (!pool_dev || !aligned(pool_dev, 2) || num_blocks < 1 || num_blocks >= (1ll << 31) ||
+      !block_table_dev || !aligned(block_table_dev, 4))
+    return CG_ERR_INVALID_ARG;
+  a.pool = pool_dev;
+  a.num_blocks = num_blocks;
+  a.block_table = block_table_dev;
+  hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(status_dev), 0, 1, stream);
+  if (e != hipSuccess) return CG_ERR_HIP;
+  return hip_status(launch_decode(a, true, stream));
+}
+
+cg_status cg_copy(void* dst_dev, const void* src_dev, uint64_t bytes, hipStream_t stream) {
+  if (!dst_dev || !src_dev || bytes % 16 != 0 || !aligned(dst_dev, 16) || !aligned(src_dev, 16))
+    return CG_ERR_INVALID_ARG;
+  return hip_status(launch_copy(dst_dev, src_dev, bytes, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,195 @@
+// cg_layout.h -- byte layouts and launch-argument structs of the gfx950 codec
+// library. Internal to the library (host API and kernels).
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/cg.h"
+
+namespace cg {
+
+constexpr uint32_t kTableMagic = 0x42544743u;   // "CGTB"
+constexpr uint32_t kRecordMagic = 0x4B434743u;  // "CGCK"
+constexpr uint32_t kVersion = 1;
+constexpr int kLanes = 64;           // channels per group = wavefront width
+constexpr int kHdrWords = 192;       // state hi, state lo, raw q0: 3 x 64 words
+constexpr uint32_t kM = 4096;        // 12-bit frequency total
+constexpr uint32_t kL = 65536;       // rANS state lower bound
+constexpr int kEsc = 255;
+constexpr int kMaxLevels = 8;
+constexpr int kMaxGroups = 255;
+constexpr int kMaxLayers = 1024;
+
+// Decoder table per channel in LDS/HBM: 128 bitmap words, 128 rank bases,
+// 256 rank -> (symbol, f-1, b) entries. 512 dwords; padded to 513 in LDS.
+constexpr int kDecDwords = 512;
+constexpr int kDecLdsStride = 513;
+// Encoder table per channel: 256 dwords (f | b << 16), padded to 257 in LDS.
+constexpr int kEncDwords = 256;
+constexpr int kEncLdsStride = 257;
+// Decoder ring buffer per wavefront: 512 16-bit words, refilled 256 at a time.
+constexpr int kRingWords = 512;
+constexpr int kWaves = 16;  // wavefronts per workgroup of the codec kernels
+
+__host__ __device__ inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+// ---- tables blob -----------------------------------------------------------
+__host__ __device__ inline uint64_t tb_f_offset(int L, int G) {
+  return align_up(64 + 4 * (uint64_t)G + (uint64_t)L, 256);
+}
+__host__ __device__ inline uint64_t tb_n_tables(int G, int H, int D) {
+  return (uint64_t)G * 2 * H * D;
+}
+__host__ __device__ inline uint64_t tb_format_bytes(int L, int H, int D, int G) {
+  return tb_f_offset(L, G) + tb_n_tables(G, H, D) * 512;
+}
+// Lookup section (not part of the format): per-group fast-quotient flags,
+// encoder tables, decoder tables.
+__host__ __device__ inline uint64_t tb_acc_offset(int L, int H, int D, int G) {
+  return align_up(tb_format_bytes(L, H, D, G), 256);
+}
+__host__ __device__ inline uint64_t tb_qflag_offset(int L, int H, int D, int G) {
+  return tb_acc_offset(L, H, D, G);
+}
+__host__ __device__ inline uint64_t tb_enc_offset(int L, int H, int D, int G) {
+  return tb_acc_offset(L, H, D, G) + 1024;
+}
+__host__ __device__ inline uint64_t tb_dec_offset(int L, int H, int D, int G) {
+  return tb_enc_offset(L, H, D, G) + tb_n_tables(G, H, D) * kEncDwords * 4;
+}
+__host__ __device__ inline uint64_t tb_total_bytes(int L, int H, int D, int G) {
+  return tb_dec_offset(L, H, D, G) + tb_n_tables(G, H, D) * kDecDwords * 4;
+}
+
+// ---- chunk records ---------------------------------------------------------
+__host__ __device__ inline int64_t n_chunks(int64_t T, int C) { return (T + C - 1) / C; }
+__host__ __device__ inline int64_t chunk_len(int64_t T, int C, int64_t c) {
+  int64_t n = T - c * C;
+  return n < C ? n : C;
+}
+__host__ __device__ inline int64_t groups_per_chunk(int L, int H, int D) {
+  return (int64_t)L * 2 * H * (D / 64);
+}
+__host__ __device__ inline uint64_t rec_data_start(int64_t gpc) {
+  return align_up(64 + 8 * (uint64_t)(gpc + 1) + 4 * (uint64_t)gpc, 256);
+}
+// Worst case words of one group of n tokens: one renorm word and one escape
+// word per symbol plus the 192-word head.
+__host__ __device__ inline uint64_t group_cap_words(int64_t n) {
+  return (uint64_t)kLanes * (2 * (uint64_t)(n - 1) + 3);
+}
+
+struct Shape {
+  int L, H, D, C, S;  // S = D / 64 slices
+  int64_t T;
+};
+
+// ---- launch arguments --------------------------------------------------------
+struct BlobInitArgs {
+  uint8_t* blob;
+  int L, H, D, G, C;
+  int32_t level_id;
+  int64_t T;
+  float step[kMaxGroups + 1];
+  uint8_t lg[kMaxLayers];
+};
+
+struct QCheckArgs {
+  const uint8_t* blob;
+  uint32_t* qflags;
+  int L, G;
+};
+
+struct HistArgs {
+  Shape s;
+  const uint16_t* x;
+  const uint8_t* blob;
+  uint32_t* counts;      // [G][2][H][D][256]
+  unsigned long long* stats;  // optional [4]
+  int G;
+};
+
+struct NormArgs {
+  const uint32_t* counts;
+  uint8_t* blob;
+  uint64_t f_off, enc_off, dec_off;
+  int64_t n_tables;
+};
+
+struct EncodeArgs {
+  Shape s;
+  const uint16_t* x;
+  const uint8_t* blob;
+  int G;
+  int64_t chunk_begin, n_chunks;
+  uint64_t cap_words;          // per group slot in the scratch
+  uint16_t* scratch;           // [n_chunks][gpc][cap_words]
+  uint32_t* group_words;       // [n_chunks][gpc]
+  uint32_t* group_start;       // [n_chunks][gpc]
+  int32_t* status;
+};
+
+struct LayoutArgs {
+  int64_t gpc;
+  int64_t n_chunks;
+  const uint32_t* group_words;
+  uint64_t* group_off;         // [n_chunks][gpc+1]
+  uint64_t* rec_bytes;         // [n_chunks]
+};
+
+struct ChunkScanArgs {
+  int64_t n_chunks;
+  const uint64_t* rec_bytes;
+  uint64_t* chunk_offsets;     // [n_chunks+1]
+  uint64_t out_cap;
+  int32_t* status;
+};
+
+struct WriteArgs {
+  Shape s;
+  int64_t gpc, chunk_begin, n_chunks;
+  const uint8_t* blob;
+  uint64_t cap_words;
+  const uint16_t* scratch;
+  const uint32_t* group_words;
+  const uint32_t* group_start;
+  const uint64_t* group_off;
+  const uint64_t* rec_bytes;
+  const uint64_t* chunk_offsets;
+  uint8_t* out;
+  uint64_t out_cap;
+  int groups_per_block;
+};
+
+struct DecodeArgs {
+  Shape s;
+  const cg_chunk_ref* refs;
+  int32_t n_refs;
+  int32_t n_tables;
+  int32_t g_max;
+  const uint8_t* tables[kMaxLevels];
+  int32_t level_id[kMaxLevels];
+  int32_t n_groups[kMaxLevels];
+  uint16_t* y;            // contiguous output (or null)
+  uint16_t* pool;         // paged output (or null)
+  int64_t num_blocks;
+  const int32_t* block_table;
+  int32_t* status;
+};
+
+// Launchers (defined next to the kernels).
+hipError_t launch_fill_u32(uint32_t* p, uint32_t value, uint64_t n, hipStream_t st);
+hipError_t launch_blob_init(const BlobInitArgs& a, hipStream_t st);
+hipError_t launch_qcheck(const QCheckArgs& a, hipStream_t st);
+hipError_t launch_hist(const HistArgs& a, hipStream_t st);
+hipError_t launch_norm(const NormArgs& a, hipStream_t st);
+hipError_t launch_encode(const EncodeArgs& a, hipStream_t st);
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t st);
+hipError_t launch_chunk_scan(const ChunkScanArgs& a, hipStream_t st);
+hipError_t launch_write(const WriteArgs& a, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, bool paged, hipStream_t st);
+hipError_t launch_make_refs(const uint8_t* base, const uint64_t* offs, int32_t n, int32_t table,
+                            cg_chunk_ref* refs, hipStream_t st);
+hipError_t launch_copy(void* dst, const void* src, uint64_t bytes, hipStream_t st);
+
+}  // namespace cg

@@ -1,0 +1,49 @@
+"""Shared plumbing of the GPU tests: run the HIP path and the oracle on the
+same seeded inputs."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from kv_cache_compression_encode_amd import cg as C  # noqa: E402
+from kv_cache_compression_encode_amd import codec  # noqa: E402
+from oracle import oracle as O  # noqa: E402
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    C.lib()  # fails loudly when libcg.so is missing
+
+
+def to_dev(X):
+    return torch.from_numpy(np.ascontiguousarray(X).view(np.int16)).to("cuda").view(torch.float16)
+
+
+def u8(t):
+    return t.detach().cpu().numpy().view(np.uint8) if t.dtype == torch.uint8 else \
+        t.detach().cpu().contiguous().view(torch.uint8).numpy()
+
+
+def gpu_roundtrip(L, H, D, T, Cc, lg, steps, X, level_id=1):
+    shp = C.shape(L, H, D, T, Cc)
+    lv = C.Level(level_id, lg, steps)
+    cd = codec.Codec(shp)
+    x = to_dev(X)
+    stats = torch.zeros(4, dtype=torch.int64, device="cuda")
+    tables = cd.build_tables(x, lv, stats=stats)
+    out, offs = cd.encode(x, lv, tables)
+    st_enc = cd.read_status()
+    refs, n = cd.refs_for(out, offs)
+    y = cd.decode([lv], [tables], refs, n)
+    st_dec = cd.read_status()
+    return dict(shp=shp, lv=lv, cd=cd, x=x, tables=tables, stats=stats, out=out, offs=offs,
+                y=y, st_enc=st_enc, st_dec=st_dec)
+
+
+def oracle_roundtrip(L, H, D, T, Cc, lg, steps, X, level_id=1):
+    oshp = O.shape(L, H, D, T, Cc)
+    blob, stats = O.build_tables(oshp, level_id, lg, steps, X)
+    data, offs = O.encode_all(oshp, blob, X)
+    Y = O.decode_all(oshp, blob, data, offs)
+    return dict(shp=oshp, blob=blob, stats=stats, data=data, offs=offs, Y=Y)
