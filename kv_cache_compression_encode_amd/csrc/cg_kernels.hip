@@ -111,6 +111,15 @@ __device__ __forceinline__ int32_t quantize(uint16_t xh, float step, float rcp, 
   return (int32_t)r;
 }
 
+// x_hat = fp16_RNE(fl32(q * step)): two roundings. The empty asm keeps the
+// binary32 product as a value; without it the backend may fuse multiply and
+// conversion into v_fma_mixlo_f16, which rounds once and differs on ties.
+__device__ __forceinline__ uint16_t dequantize(int32_t q, float step) {
+  float v = (float)q * step;
+  asm volatile("" : "+v"(v));
+  return f2h(v);
+}
+
 __device__ __forceinline__ int32_t wrap16(int32_t v) { return ((v + 32768) & 0xFFFF) - 32768; }
 
 __device__ __forceinline__ uint32_t symbol_of(int32_t d) {
@@ -704,14 +713,14 @@ __device__ __forceinline__ void decode_group(const DecodeArgs& a, const uint32_t
   if (!PAGED) {
     yp = a.y + ((((size_t)l * 2 + kv) * s.H + h) * (size_t)s.T + t0) * s.D + 64 * j + lane;
     ystride = (size_t)s.D;
-    yp[0] = f2h((float)q * step);
+    yp[0] = dequantize(q, step);
   }
   const size_t pool_base = PAGED ? (((size_t)l * 2 + kv) * (size_t)a.num_blocks) : 0;
   auto pool_ptr = [&](int64_t t) -> uint16_t* {
     const int32_t blk = __builtin_amdgcn_readfirstlane(a.block_table[t >> 4]);
     return a.pool + (((pool_base + (size_t)blk) * s.H + h) * 16 + (size_t)(t & 15)) * s.D + 64 * j + lane;
   };
-  if (PAGED) *pool_ptr(t0) = f2h((float)q * step);
+  if (PAGED) *pool_ptr(t0) = dequantize(q, step);
 
   for (int64_t i = 1; i < n; ++i) {
     if (loaded - p < 256u) {
@@ -739,7 +748,7 @@ __device__ __forceinline__ void decode_group(const DecodeArgs& a, const uint32_t
       p += (uint32_t)__popcll(me);
     }
     q = (int32_t)(int16_t)(q + d);
-    const uint16_t y = f2h((float)q * step);
+    const uint16_t y = dequantize(q, step);
     if (PAGED) {
       *pool_ptr(t0 + i) = y;
     } else {

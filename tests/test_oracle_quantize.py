@@ -73,6 +73,15 @@ def test_error_bound_all_halves(step):
     assert np.all(err[fin] <= np.float64(np.float32(step)) / 2 + ulp[fin] + 1e-12)
 
 
+def test_dequant_rounds_twice():
+    """fl32(1035 * 1.1f) is exactly 1138.5, a tie in binary16 that goes to the
+    even 1138; a single rounding of the exact product (1138.50002...) would
+    give 1139."""
+    assert np.float32(1035) * np.float32(1.1) == np.float32(1138.5)
+    assert O.dequantize(1035, 1.1) == int(np.float16(1138).view(np.uint16))
+    assert O.dequantize(-1035, 1.1) == int(np.float16(-1138).view(np.uint16))
+
+
 def test_integer_identity_step_one():
     x = np.arange(-2048, 2049).astype(np.float16).view(np.uint16)
     q = O.quantize_array(x, 1.0)
