@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of the gfx950 KV-cache codec on one MI355X.
+
+One step = one pass of the whole hot path over the workload already resident
+in HBM: cg_build_tables (quantize + delta + per-channel histograms + 12-bit
+tables), cg_encode (interleaved rANS + record compaction) and cg_decode
+(fused rANS decode + token prefix + dequantize into the contiguous cache).
+
+value = fp16 bytes of the KV cache / seconds per step (round trip). The JSON
+line also carries decode / encode / table-build GB/s, the compression ratio,
+the roofline of the dominant kernel and the CPU oracle timed on a sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV decode & encode GB/s (fp16 bytes) on 1 MI355X; % HBM peak; compression ratio"
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, X, seconds=10.0):
+    """The oracle (single thread) on a bounded sample of the same workload:
+    layer 0, all heads, the first two chunks; build + encode + decode."""
+    import numpy as np
+
+    from oracle import oracle as O
+
+    lvd = cfg.levels[0]
+    T = min(cfg.tokens, 2 * cfg.chunk_tokens)
+    Xs = np.ascontiguousarray(X[:1, :, :, :T, :])
+    shp = O.shape(1, cfg.kv_heads, cfg.head_dim, T, cfg.chunk_tokens)
+    steps = [lvd.steps[lvd.layer_group[0]]]
+    elems = 0
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        blob, _ = O.build_tables(shp, lvd.level_id, [0], steps, Xs)
+        data, offs = O.encode_all(shp, blob, Xs)
+        O.decode_all(shp, blob, data, offs)
+        elems += Xs.size
+        reps += 1
+        if time.perf_counter() - t0 >= seconds or reps >= 50:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(2 * elems / dt / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "layer 0 of the workload, %d tokens (%d chunks), all heads: build tables + "
+                      "encode + decode, %d repetition(s), %.1f s single-threaded" % (
+                          T, -(-T // cfg.chunk_tokens), reps, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="34b", help="tiny | 7b | 34b (workload of the step)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="per-launch HBM bytes of the dominant kernel from rocprofv3 counters")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from kv_cache_compression_encode_amd import cg as C
+    from kv_cache_compression_encode_amd import codec, synth
+
+    C.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = synth.CONFIGS[args.config]
+    lvd = cfg.levels[0]
+    t_gen = time.perf_counter()
+    X = synth.generate(cfg)
+    log("generated %s %s in %.1f s" % (cfg.name, X.shape, time.perf_counter() - t_gen))
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.float16)
+    N = x.numel()
+    fp16_bytes = 2 * N
+
+    shp = codec.shape_of(cfg)
+    lv = codec.level_of(lvd)
+    cd = codec.Codec(shp, dev)
+    nch = codec.n_chunks(shp)
+    tables = torch.empty(cd.tables_bytes(lv), dtype=torch.uint8, device=dev)
+    out = torch.empty(C.cg_encode_bound(shp, 0, nch), dtype=torch.uint8, device=dev)
+    offs = torch.zeros(nch + 1, dtype=torch.int64, device=dev)
+    y = torch.empty_like(x)
+    refs = torch.empty(nch * C.REF_BYTES, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        cd.build_tables(x, lv, tables=tables)
+        if ev:
+            ev[1].record(stream)
+        cd.encode(x, lv, tables, out=out, offsets=offs)
+        if ev:
+            ev[2].record(stream)
+        C.cg_make_refs(out, offs, nch, 0, refs)
+        if ev:
+            ev[3].record(stream)
+        cd.decode([lv], [tables], refs, nch, y=y)
+        if ev:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert cd.read_status() == 0, "codec reported status %d" % cd.read_status()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = cd.read_status()
+    assert st == 0, "codec reported status %d" % st
+
+    ms = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in events])
+    t_build, t_enc, t_refs, t_dec = ms.mean(axis=0)
+    comp = int(offs[-1].item())
+    fmt = cd.format_bytes(lv)
+    ratio = fp16_bytes / comp
+    # correctness of this very run: the decoded cache equals numpy's
+    # dequant(quant(x)) on sampled (layer, K|V, head) slices
+    rng = np.random.default_rng(0)
+    bad = 0
+    for _ in range(4):
+        l, kv, h = int(rng.integers(cfg.layers)), int(rng.integers(2)), int(rng.integers(cfg.kv_heads))
+        step_ = np.float32(lvd.steps[lvd.layer_group[l]])
+        xs = X[l, kv, h].astype(np.float64)
+        with np.errstate(all="ignore"):
+            q = np.clip(np.rint((xs / np.float64(step_)).astype(np.float32)), -32768, 32767)
+            ref = (q.astype(np.float32) * step_).astype(np.float16).view(np.uint16)
+        got = y[l, kv, h].cpu().numpy().view(np.uint16)
+        bad += int(np.count_nonzero(got != ref))
+    assert bad == 0, "decoded values differ from the reference reconstruction"
+
+    # dominant kernel of the step and its roofline
+    n_tables = 2 * lv.n_groups * cfg.kv_heads * cfg.head_dim
+    dec_tables = n_tables * 2048
+    phases = {
+        "k_hist (cg_build_tables)": (t_build, fp16_bytes + fmt),
+        "k_encode (cg_encode)": (t_enc, fp16_bytes + comp),
+        "k_decode (cg_decode)": (t_dec, fp16_bytes + comp + dec_tables),
+    }
+    dom = max(phases, key=lambda k: phases[k][0])
+
+    def roof(name):
+        t, b = phases[name]
+        gbps = b / (t / 1e3) / 1e9
+        r = {"kernel": name, "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+             "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+             "algorithmic_bytes": int(b), "avg_ms": round(float(t), 4)}
+        try:
+            tr = json.load(open(args.traffic))
+            ent = tr.get(args.config, {}).get(name.split()[0])
+            if ent and ent.get("source_hash") == tr.get("kernel_source_hash"):
+                r["traffic"] = ent["bytes_per_launch"]
+        except (OSError, ValueError):
+            pass
+        return r
+
+    res = {
+        "metric": METRIC,
+        "value": round(fp16_bytes / (wall / args.steps) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 data; fp32 quantize/dequantize, u32 rANS",
+        "data": "synthetic",
+        "config": {"workload": "%s: %d layers x %d KV heads x %d dim x %d tokens, fp16 K+V, chunk %d, "
+                               "%s steps %s" % (cfg.name, cfg.layers, cfg.kv_heads, cfg.head_dim,
+                                                cfg.tokens, cfg.chunk_tokens, lvd.name,
+                                                "/".join(str(s) for s in lvd.steps)),
+                   "fp16_bytes": fp16_bytes, "chunks": nch},
+        "decode_GBps": round(fp16_bytes / (t_dec / 1e3) / 1e9, 1),
+        "encode_GBps": round(fp16_bytes / (t_enc / 1e3) / 1e9, 1),
+        "build_tables_GBps": round(fp16_bytes / (t_build / 1e3) / 1e9, 1),
+        "decode_ms": round(float(t_dec), 4),
+        "encode_ms": round(float(t_enc), 4),
+        "build_tables_ms": round(float(t_build), 4),
+        "compressed_bytes": comp,
+        "compression_ratio": round(ratio, 3),
+        "compressed_fraction": round(comp / fp16_bytes, 4),
+        "ratio_incl_tables": round(fp16_bytes / (comp + fmt), 3),
+        "roofline": roof(dom),
+        "roofline_decode": roof("k_decode (cg_decode)"),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, X, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
