@@ -104,19 +104,20 @@ def main():
     refs = torch.empty(nch * C.REF_BYTES, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def step(ev=None, kt=None):
+        kt = kt or {}
         if ev:
             ev[0].record(stream)
-        cd.build_tables(x, lv, tables=tables)
+        cd.build_tables(x, lv, tables=tables, prof=kt.get("build"))
         if ev:
             ev[1].record(stream)
-        cd.encode(x, lv, tables, out=out, offsets=offs)
+        cd.encode(x, lv, tables, out=out, offsets=offs, prof=kt.get("encode"))
         if ev:
             ev[2].record(stream)
         C.cg_make_refs(out, offs, nch, 0, refs)
         if ev:
             ev[3].record(stream)
-        cd.decode([lv], [tables], refs, nch, y=y)
+        cd.decode([lv], [tables], refs, nch, y=y, prof=kt.get("decode"))
         if ev:
             ev[4].record(stream)
 
@@ -125,17 +126,20 @@ def main():
     torch.cuda.synchronize()
     assert cd.read_status() == 0, "codec reported status %d" % cd.read_status()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    timers = [{k: C.KernelTimer() for k in ("build", "encode", "decode")} for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(events[k])
+        step(events[k], timers[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     st = cd.read_status()
     assert st == 0, "codec reported status %d" % st
 
+    # per call (all kernels of the call) and per main kernel, mean over the steps
     ms = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in events])
     t_build, t_enc, t_refs, t_dec = ms.mean(axis=0)
+    kms = {k: float(np.mean([t[k].elapsed_ms() for t in timers])) for k in ("build", "encode", "decode")}
     comp = int(offs[-1].item())
     fmt = cd.format_bytes(lv)
     ratio = fp16_bytes / comp
@@ -149,6 +153,7 @@ def main():
         xs = X[l, kv, h].astype(np.float64)
         with np.errstate(all="ignore"):
             q = np.clip(np.rint((xs / np.float64(step_)).astype(np.float32)), -32768, 32767)
+            q = np.nan_to_num(q).astype(np.int32)  # an integer code: no signed zero
             ref = (q.astype(np.float32) * step_).astype(np.float16).view(np.uint16)
         got = y[l, kv, h].cpu().numpy().view(np.uint16)
         bad += int(np.count_nonzero(got != ref))
@@ -158,9 +163,9 @@ def main():
     n_tables = 2 * lv.n_groups * cfg.kv_heads * cfg.head_dim
     dec_tables = n_tables * 2048
     phases = {
-        "k_hist (cg_build_tables)": (t_build, fp16_bytes + fmt),
-        "k_encode (cg_encode)": (t_enc, fp16_bytes + comp),
-        "k_decode (cg_decode)": (t_dec, fp16_bytes + comp + dec_tables),
+        "k_hist": (kms["build"], fp16_bytes + fmt),
+        "k_encode": (kms["encode"], fp16_bytes + comp),
+        "k_decode": (kms["decode"], fp16_bytes + comp + dec_tables),
     }
     dom = max(phases, key=lambda k: phases[k][0])
 
@@ -172,7 +177,7 @@ def main():
              "algorithmic_bytes": int(b), "avg_ms": round(float(t), 4)}
         try:
             tr = json.load(open(args.traffic))
-            ent = tr.get(args.config, {}).get(name.split()[0])
+            ent = tr.get(args.config, {}).get(name)
             if ent and ent.get("source_hash") == tr.get("kernel_source_hash"):
                 r["traffic"] = ent["bytes_per_launch"]
         except (OSError, ValueError):
@@ -208,7 +213,9 @@ def main():
         "compressed_fraction": round(comp / fp16_bytes, 4),
         "ratio_incl_tables": round(fp16_bytes / (comp + fmt), 3),
         "roofline": roof(dom),
-        "roofline_decode": roof("k_decode (cg_decode)"),
+        "roofline_decode": roof("k_decode"),
+        "kernel_ms": {"k_hist": round(kms["build"], 4), "k_encode": round(kms["encode"], 4),
+                      "k_decode": round(kms["decode"], 4)},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, X, args.cpu_seconds)

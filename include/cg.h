@@ -88,6 +88,15 @@ typedef struct cg_chunk_ref {
   int32_t reserved;      /* 0                                                             */
 } cg_chunk_ref;
 
+/* Optional timing hook. When a call gets a non-null cg_profile, it records
+ * main_begin right before and main_end right after its main kernel (k_hist for
+ * cg_build_tables, k_encode for cg_encode, k_decode for the decoders) on the
+ * call's stream. The events are created and owned by the caller. */
+typedef struct cg_profile {
+  hipEvent_t main_begin;
+  hipEvent_t main_end;
+} cg_profile;
+
 /* Library version (1) and a readable name for a status code. */
 int32_t cg_version(void);
 const char* cg_status_string(cg_status s);
@@ -117,7 +126,7 @@ size_t cg_build_workspace_bytes(const cg_shape* shape, int32_t n_groups);
  * Data errors: none. */
 cg_status cg_build_tables(const cg_shape* shape, const cg_level* level, const uint16_t* x_dev,
                           void* tables_dev, void* ws_dev, size_t ws_bytes, uint64_t* stats_dev,
-                          hipStream_t stream);
+                          const cg_profile* prof, hipStream_t stream);
 
 /* ---- encode -------------------------------------------------------------- */
 
@@ -144,7 +153,7 @@ cg_status cg_encode(const cg_shape* shape, const cg_level* level, const void* ta
                     const uint16_t* x_dev,
                     int64_t chunk_begin, int64_t chunk_end, uint8_t* out_dev, uint64_t out_cap,
                     uint64_t* chunk_offsets_dev, void* ws_dev, size_t ws_bytes,
-                    int32_t* status_dev, hipStream_t stream);
+                    int32_t* status_dev, const cg_profile* prof, hipStream_t stream);
 
 /* Fills refs_dev[i] = {base_dev + offsets_dev[i], offsets_dev[i+1] - offsets_dev[i],
  * table, 0} for i < n (a helper to decode what cg_encode wrote). */
@@ -164,7 +173,8 @@ cg_status cg_make_refs(const uint8_t* base_dev, const uint64_t* offsets_dev, int
  * out of range, blob not matching its level). */
 cg_status cg_decode(const cg_shape* shape, int32_t n_levels, const cg_level* levels,
                     const void* const* tables_dev, const cg_chunk_ref* refs_dev, int32_t n_refs,
-                    uint16_t* y_dev, int32_t* status_dev, hipStream_t stream);
+                    uint16_t* y_dev, int32_t* status_dev, const cg_profile* prof,
+                    hipStream_t stream);
 
 /* As cg_decode, but the destination is a paged cache: token t of layer l,
  * K|V kv, head h goes to pool_dev[l][kv][block_table_dev[t/16]][h][t%16][:]
@@ -177,7 +187,7 @@ cg_status cg_decode_paged(const cg_shape* shape, int32_t n_levels, const cg_leve
                           const void* const* tables_dev, const cg_chunk_ref* refs_dev,
                           int32_t n_refs, uint16_t* pool_dev, int64_t num_blocks,
                           const int32_t* block_table_dev, int32_t* status_dev,
-                          hipStream_t stream);
+                          const cg_profile* prof, hipStream_t stream);
 
 /* ---- measurement helper ---------------------------------------------------- */
 

@@ -44,7 +44,54 @@ class cg_chunk_ref(ctypes.Structure):
                 ("table", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
+class cg_profile(ctypes.Structure):
+    _fields_ = [("main_begin", ctypes.c_void_p), ("main_end", ctypes.c_void_p)]
+
+
 REF_BYTES = ctypes.sizeof(cg_chunk_ref)  # 24
+
+_hip = None
+
+
+def hip():
+    """The HIP runtime (already loaded by torch), for events only."""
+    global _hip
+    if _hip is None:
+        h = ctypes.CDLL("libamdhip64.so")
+        h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        _hip = h
+    return _hip
+
+
+class KernelTimer:
+    """Two HIP events a call records around its main kernel (cg_profile)."""
+
+    def __init__(self):
+        a, b = ctypes.c_void_p(), ctypes.c_void_p()
+        if hip().hipEventCreate(ctypes.byref(a)) or hip().hipEventCreate(ctypes.byref(b)):
+            raise RuntimeError("hipEventCreate failed")
+        self.c = cg_profile(a.value, b.value)
+
+    def elapsed_ms(self) -> float:
+        hip().hipEventSynchronize(self.c.main_end)
+        ms = ctypes.c_float()
+        if hip().hipEventElapsedTime(ctypes.byref(ms), self.c.main_begin, self.c.main_end):
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        try:
+            hip().hipEventDestroy(self.c.main_begin)
+            hip().hipEventDestroy(self.c.main_end)
+        except Exception:
+            pass
+
+
+def _prof(p):
+    return ctypes.byref(p.c) if p is not None else None
 
 
 class Level:
@@ -74,19 +121,20 @@ def lib():
     L = ctypes.CDLL(LIB)
     P, i32, i64, u64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t
     sp, lp = ctypes.POINTER(cg_shape), ctypes.POINTER(cg_level)
+    pp = ctypes.POINTER(cg_profile)
     sigs = {
         "cg_version": (i32, []),
         "cg_status_string": (ctypes.c_char_p, [i32]),
         "cg_tables_bytes": (sz, [sp, i32]),
         "cg_tables_format_bytes": (sz, [sp, i32]),
         "cg_build_workspace_bytes": (sz, [sp, i32]),
-        "cg_build_tables": (i32, [sp, lp, P, P, P, sz, P, P]),
+        "cg_build_tables": (i32, [sp, lp, P, P, P, sz, P, pp, P]),
         "cg_encode_bound": (sz, [sp, i64, i64]),
         "cg_encode_workspace_bytes": (sz, [sp, i64, i64]),
-        "cg_encode": (i32, [sp, lp, P, P, i64, i64, P, u64, P, P, sz, P, P]),
+        "cg_encode": (i32, [sp, lp, P, P, i64, i64, P, u64, P, P, sz, P, pp, P]),
         "cg_make_refs": (i32, [P, P, i32, i32, P, P]),
-        "cg_decode": (i32, [sp, i32, lp, P, P, i32, P, P, P]),
-        "cg_decode_paged": (i32, [sp, i32, lp, P, P, i32, P, i64, P, P, P]),
+        "cg_decode": (i32, [sp, i32, lp, P, P, i32, P, P, pp, P]),
+        "cg_decode_paged": (i32, [sp, i32, lp, P, P, i32, P, i64, P, P, pp, P]),
         "cg_copy": (i32, [P, P, u64, P]),
     }
     for name, (res, args) in sigs.items():
@@ -153,9 +201,10 @@ def cg_build_workspace_bytes(shp: cg_shape, n_groups: int) -> int:
     return lib().cg_build_workspace_bytes(ctypes.byref(shp), n_groups)
 
 
-def cg_build_tables(shp, level: Level, x, tables, ws, stats=None, stream=None):
+def cg_build_tables(shp, level: Level, x, tables, ws, stats=None, prof=None, stream=None):
     rc = lib().cg_build_tables(ctypes.byref(shp), ctypes.byref(level.c), _ptr(x), _ptr(tables),
-                               _ptr(ws), ws.numel() * ws.element_size(), _ptr(stats), _stream(stream))
+                               _ptr(ws), ws.numel() * ws.element_size(), _ptr(stats), _prof(prof),
+                               _stream(stream))
     _check("cg_build_tables", rc)
 
 
@@ -168,11 +217,11 @@ def cg_encode_workspace_bytes(shp, chunk_begin, chunk_end) -> int:
 
 
 def cg_encode(shp, level: Level, tables, x, chunk_begin, chunk_end, out, chunk_offsets, ws, status,
-              stream=None):
+              prof=None, stream=None):
     rc = lib().cg_encode(ctypes.byref(shp), ctypes.byref(level.c), _ptr(tables), _ptr(x),
                          chunk_begin, chunk_end, _ptr(out), out.numel() * out.element_size(),
                          _ptr(chunk_offsets), _ptr(ws), ws.numel() * ws.element_size(), _ptr(status),
-                         _stream(stream))
+                         _prof(prof), _stream(stream))
     _check("cg_encode", rc)
 
 
@@ -187,19 +236,19 @@ def _levels_and_tables(levels, tables):
     return arr, tp
 
 
-def cg_decode(shp, levels, tables, refs, n_refs, y, status, stream=None):
+def cg_decode(shp, levels, tables, refs, n_refs, y, status, prof=None, stream=None):
     arr, tp = _levels_and_tables(levels, tables)
     rc = lib().cg_decode(ctypes.byref(shp), len(levels), arr, tp, _ptr(refs), int(n_refs), _ptr(y),
-                         _ptr(status), _stream(stream))
+                         _ptr(status), _prof(prof), _stream(stream))
     _check("cg_decode", rc)
 
 
 def cg_decode_paged(shp, levels, tables, refs, n_refs, pool, num_blocks, block_table, status,
-                    stream=None):
+                    prof=None, stream=None):
     arr, tp = _levels_and_tables(levels, tables)
     rc = lib().cg_decode_paged(ctypes.byref(shp), len(levels), arr, tp, _ptr(refs), int(n_refs),
                                _ptr(pool), int(num_blocks), _ptr(block_table), _ptr(status),
-                               _stream(stream))
+                               _prof(prof), _stream(stream))
     _check("cg_decode_paged", rc)
 
 

@@ -54,15 +54,16 @@ class Codec:
     def format_bytes(self, level: C.Level) -> int:
         return C.cg_tables_format_bytes(self.shp, level.n_groups)
 
-    def build_tables(self, x: torch.Tensor, level: C.Level, tables=None, stats=None):
+    def build_tables(self, x: torch.Tensor, level: C.Level, tables=None, stats=None, prof=None):
         if tables is None:
             tables = _bytes(self.tables_bytes(level), self.device)
         ws = self._workspace("build", C.cg_build_workspace_bytes(self.shp, level.n_groups))
-        C.cg_build_tables(self.shp, level, x, tables, ws, stats)
+        C.cg_build_tables(self.shp, level, x, tables, ws, stats, prof)
         return tables
 
     # -- encode -------------------------------------------------------------
-    def encode(self, x, level, tables, chunk_begin=0, chunk_end=None, out=None, offsets=None):
+    def encode(self, x, level, tables, chunk_begin=0, chunk_end=None, out=None, offsets=None,
+               prof=None):
         """Records of chunks [chunk_begin, chunk_end) -> (out bytes, offsets u64 [n+1])."""
         if chunk_end is None:
             chunk_end = n_chunks(self.shp)
@@ -72,7 +73,8 @@ class Codec:
         if offsets is None:
             offsets = torch.zeros(n + 1, dtype=torch.int64, device=self.device)
         ws = self._workspace("encode", C.cg_encode_workspace_bytes(self.shp, chunk_begin, chunk_end))
-        C.cg_encode(self.shp, level, tables, x, chunk_begin, chunk_end, out, offsets, ws, self.status)
+        C.cg_encode(self.shp, level, tables, x, chunk_begin, chunk_end, out, offsets, ws, self.status,
+                    prof)
         return out, offsets
 
     # -- decode -------------------------------------------------------------
@@ -96,14 +98,14 @@ class Codec:
         C.cg_make_refs(out, offsets, n, table, refs)
         return refs, n
 
-    def decode(self, levels, tables, refs, n_refs, y=None):
+    def decode(self, levels, tables, refs, n_refs, y=None, prof=None):
         if y is None:
             y = torch.empty((self.shp.layers, 2, self.shp.kv_heads, self.shp.tokens, self.shp.head_dim),
                             dtype=torch.float16, device=self.device)
-        C.cg_decode(self.shp, levels, tables, refs, n_refs, y, self.status)
+        C.cg_decode(self.shp, levels, tables, refs, n_refs, y, self.status, prof)
         return y
 
-    def decode_paged(self, levels, tables, refs, n_refs, pool, block_table):
+    def decode_paged(self, levels, tables, refs, n_refs, pool, block_table, prof=None):
         C.cg_decode_paged(self.shp, levels, tables, refs, n_refs, pool, pool.shape[2], block_table,
-                          self.status)
+                          self.status, prof)
         return pool

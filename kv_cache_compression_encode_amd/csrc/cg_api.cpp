@@ -52,6 +52,12 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 cg_status hip_status(hipError_t e) { return e == hipSuccess ? CG_OK : CG_ERR_HIP; }
 
+hipError_t mark(const cg_profile* prof, bool begin, hipStream_t st) {
+  if (!prof) return hipSuccess;
+  hipEvent_t ev = begin ? prof->main_begin : prof->main_end;
+  return ev ? hipEventRecord(ev, st) : hipSuccess;
+}
+
 struct EncodeWs {
   uint64_t gw, gs, go, rb, scratch, total;
 };
@@ -119,7 +125,7 @@ size_t cg_build_workspace_bytes(const cg_shape* shape, int32_t n_groups) {
 
 cg_status cg_build_tables(const cg_shape* shape, const cg_level* level, const uint16_t* x_dev,
                           void* tables_dev, void* ws_dev, size_t ws_bytes, uint64_t* stats_dev,
-                          hipStream_t stream) {
+                          const cg_profile* prof, hipStream_t stream) {
   Shape s;
   cg_status rc = check_shape(shape, &s);
   if (rc != CG_OK) return rc;
@@ -168,7 +174,9 @@ cg_status cg_build_tables(const cg_shape* shape, const cg_level* level, const ui
   ha.counts = counts;
   ha.stats = reinterpret_cast<unsigned long long*>(stats_dev);
   ha.G = G;
+  if ((e = mark(prof, true, stream)) != hipSuccess) return CG_ERR_HIP;
   if ((e = launch_hist(ha, stream)) != hipSuccess) return CG_ERR_HIP;
+  if ((e = mark(prof, false, stream)) != hipSuccess) return CG_ERR_HIP;
 
   NormArgs na;
   na.counts = counts;
@@ -202,7 +210,8 @@ size_t cg_encode_workspace_bytes(const cg_shape* shape, int64_t chunk_begin, int
 cg_status cg_encode(const cg_shape* shape, const cg_level* level, const void* tables_dev,
                     const uint16_t* x_dev, int64_t chunk_begin, int64_t chunk_end,
                     uint8_t* out_dev, uint64_t out_cap, uint64_t* chunk_offsets_dev, void* ws_dev,
-                    size_t ws_bytes, int32_t* status_dev, hipStream_t stream) {
+                    size_t ws_bytes, int32_t* status_dev, const cg_profile* prof,
+                    hipStream_t stream) {
   Shape s;
   cg_status rc = check_shape(shape, &s);
   if (rc != CG_OK) return rc;
@@ -238,7 +247,9 @@ cg_status cg_encode(const cg_shape* shape, const cg_level* level, const void* ta
   ea.group_words = reinterpret_cast<uint32_t*>(ws + w.gw);
   ea.group_start = reinterpret_cast<uint32_t*>(ws + w.gs);
   ea.status = status_dev;
+  if ((e = mark(prof, true, stream)) != hipSuccess) return CG_ERR_HIP;
   if ((e = launch_encode(ea, stream)) != hipSuccess) return CG_ERR_HIP;
+  if ((e = mark(prof, false, stream)) != hipSuccess) return CG_ERR_HIP;
 
   LayoutArgs la;
   la.gpc = gpc;
@@ -317,22 +328,25 @@ static cg_status decode_common(const cg_shape* shape, int32_t n_levels, const cg
 
 cg_status cg_decode(const cg_shape* shape, int32_t n_levels, const cg_level* levels,
                     const void* const* tables_dev, const cg_chunk_ref* refs_dev, int32_t n_refs,
-                    uint16_t* y_dev, int32_t* status_dev, hipStream_t stream) {
+                    uint16_t* y_dev, int32_t* status_dev, const cg_profile* prof,
+                    hipStream_t stream) {
   DecodeArgs a;
   cg_status rc = decode_common(shape, n_levels, levels, tables_dev, refs_dev, n_refs, status_dev, &a);
   if (rc != CG_OK) return rc;
   if (!y_dev || !aligned(y_dev, 2)) return CG_ERR_INVALID_ARG;
   a.y = y_dev;
   hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(status_dev), 0, 1, stream);
-  if (e != hipSuccess) return CG_ERR_HIP;
-  return hip_status(launch_decode(a, false, stream));
+  if (e == hipSuccess) e = mark(prof, true, stream);
+  if (e == hipSuccess) e = launch_decode(a, false, stream);
+  if (e == hipSuccess) e = mark(prof, false, stream);
+  return hip_status(e);
 }
 
 cg_status cg_decode_paged(const cg_shape* shape, int32_t n_levels, const cg_level* levels,
                           const void* const* tables_dev, const cg_chunk_ref* refs_dev,
                           int32_t n_refs, uint16_t* pool_dev, int64_t num_blocks,
                           const int32_t* block_table_dev, int32_t* status_dev,
-                          hipStream_t stream) {
+                          const cg_profile* prof, hipStream_t stream) {
   DecodeArgs a;
   cg_status rc = decode_common(shape, n_levels, levels, tables_dev, refs_dev, n_refs, status_dev, &a);
   if (rc != CG_OK) return rc;
@@ -343,8 +357,10 @@ cg_status cg_decode_paged(const cg_shape* shape, int32_t n_levels, const cg_leve
   a.num_blocks = num_blocks;
   a.block_table = block_table_dev;
   hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(status_dev), 0, 1, stream);
-  if (e != hipSuccess) return CG_ERR_HIP;
-  return hip_status(launch_decode(a, true, stream));
+  if (e == hipSuccess) e = mark(prof, true, stream);
+  if (e == hipSuccess) e = launch_decode(a, true, stream);
+  if (e == hipSuccess) e = mark(prof, false, stream);
+  return hip_status(e);
 }
 
 cg_status cg_copy(void* dst_dev, const void* src_dev, uint64_t bytes, hipStream_t stream) {
