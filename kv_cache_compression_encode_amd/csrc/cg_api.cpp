@@ -24,6 +24,9 @@ cg_status check_shape(const cg_shape* sp, Shape* out) {
       s.head_dim > (1 << 16))
     return CG_ERR_UNSUPPORTED;
   if ((uint64_t)s.layers * (uint64_t)s.tokens >= (1ull << 32)) return CG_ERR_UNSUPPORTED;
+  // per-(layer, K|V, head) slabs and per-chunk slices are addressed with
+  // 32-bit buffer offsets
+  if ((uint64_t)s.tokens * s.head_dim * 2 >= (1ull << 32)) return CG_ERR_UNSUPPORTED;
   const uint64_t gpc = (uint64_t)s.layers * 2 * s.kv_heads * (s.head_dim / 64);
   if (gpc >= (1ull << 31)) return CG_ERR_UNSUPPORTED;
   if (out) {
@@ -353,6 +356,9 @@ cg_status cg_decode_paged(const cg_shape* shape, int32_t n_levels, const cg_leve
   if (!pool_dev || !aligned(pool_dev, 2) || num_blocks < 1 || num_blocks >= (1ll << 31) ||
       !block_table_dev || !aligned(block_table_dev, 4))
     return CG_ERR_INVALID_ARG;
+  // one (layer, K|V) slab of the pool is addressed with 32-bit buffer offsets
+  if ((uint64_t)num_blocks * shape->kv_heads * 16 * shape->head_dim * 2 >= (1ull << 32))
+    return CG_ERR_UNSUPPORTED;
   a.pool = pool_dev;
   a.num_blocks = num_blocks;
   a.block_table = block_table_dev;

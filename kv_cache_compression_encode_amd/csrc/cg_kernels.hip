@@ -78,16 +78,25 @@ __device__ __forceinline__ void set_status(int32_t* status, int32_t code) {
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 __device__ __forceinline__ uint16_t f2h(float f) { return __half_as_ushort(__float2half_rn(f)); }
 
+// (float)(int16_t)v with the sign extension folded into the conversion.
+__device__ __forceinline__ float cvt_f32_sext16(int32_t v) {
+  float r;
+  asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_0"
+      : "=v"(r)
+      : "v"(v));
+  return r;
+}
+
 // q = clamp(rint_even(fl32(x / step)), -32768, 32767), NaN -> 0.
-// fast: v1 = x*r, e = x - v1*step (exact by FMA), v = v1 + e*r with r = RN(1/step);
+// FAST: v1 = x*r, e = x - v1*step (exact by FMA), v = v1 + e*r with r = RN(1/step);
 // used only for steps where k_qcheck proved it equal to the IEEE quotient for
-// every fp16 input.
-template <bool COUNT>
-__device__ __forceinline__ int32_t quantize(uint16_t xh, float step, float rcp, bool fast,
-                                            uint32_t& sat, uint32_t& nan_) {
+// every fp16 input. Branch-free; sat / nan_ count saturated and NaN inputs.
+template <bool FAST>
+__device__ __forceinline__ int32_t quantize(uint16_t xh, float step, float rcp, uint32_t& sat,
+                                            uint32_t& nan_) {
   const float x = h2f(xh);
   float v;
-  if (fast) {
+  if (FAST) {
     const float v1 = x * rcp;
     const float e = __builtin_fmaf(-v1, step, x);
     const float v2 = __builtin_fmaf(e, rcp, v1);
@@ -95,20 +104,12 @@ __device__ __forceinline__ int32_t quantize(uint16_t xh, float step, float rcp, 
   } else {
     v = x / step;
   }
-  if (v != v) {
-    if (COUNT) nan_ += 1;
-    return 0;
-  }
+  const bool is_nan = v != v;
   const float r = __builtin_rintf(v);
-  if (r > 32767.0f) {
-    if (COUNT) sat += 1;
-    return 32767;
-  }
-  if (r < -32768.0f) {
-    if (COUNT) sat += 1;
-    return -32768;
-  }
-  return (int32_t)r;
+  sat += (r > 32767.0f) | (r < -32768.0f);
+  nan_ += is_nan;
+  const float c = __builtin_fminf(__builtin_fmaxf(r, -32768.0f), 32767.0f);
+  return is_nan ? 0 : (int32_t)c;
 }
 
 // x_hat = fp16_RNE(fl32(q * step)): two roundings. The empty asm keeps the
@@ -120,10 +121,49 @@ __device__ __forceinline__ uint16_t dequantize(int32_t q, float step) {
   return f2h(v);
 }
 
+// Same, for q held modulo 2^16 in the low half of a 32-bit register.
+__device__ __forceinline__ uint16_t dequantize_low16(uint32_t q, float step) {
+  float v = cvt_f32_sext16((int32_t)q) * step;
+  asm volatile("" : "+v"(v));
+  return f2h(v);
+}
+
 __device__ __forceinline__ int32_t wrap16(int32_t v) { return ((v + 32768) & 0xFFFF) - 32768; }
 
+// d in [-127, 127] -> d + 127; anything else (as unsigned, >= 255) -> 255.
 __device__ __forceinline__ uint32_t symbol_of(int32_t d) {
-  return ((uint32_t)(d + 127) <= 254u) ? (uint32_t)(d + 127) : (uint32_t)kEsc;
+  const uint32_t u = (uint32_t)(d + 127);
+  return u < (uint32_t)kEsc ? u : (uint32_t)kEsc;
+}
+
+// mbcnt with a base: base + number of set bits of m in lanes below this one.
+__device__ __forceinline__ uint32_t mbcnt_base(uint64_t m, uint32_t base) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, base));
+}
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Values every lane loads from the same address (headers, offsets, layer
+// groups). Loads through generic pointers count as per-lane for the
+// compiler's divergence analysis; moving them to scalar registers keeps the
+// loops that depend on them uniform.
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int32_t uni(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint64_t uni(uint64_t v) {
+  return ((uint64_t)uni((uint32_t)(v >> 32)) << 32) | uni((uint32_t)v);
+}
+__device__ __forceinline__ float uni(float v) { return __uint_as_float(uni(__float_as_uint(v))); }
+template <typename T>
+__device__ __forceinline__ T* uni(T* p) {
+  return reinterpret_cast<T*>(uni((uint64_t)reinterpret_cast<uintptr_t>(p)));
+}
+
+// Raw buffer resource over [base, base + bytes): accesses use a per-lane
+// offset in a VGPR plus a wave-uniform offset in an SGPR, so address
+// arithmetic stays on the scalar unit; loads past `bytes` return 0 and stores
+// past it are dropped by the hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 struct BlobHdr {
@@ -137,9 +177,20 @@ __device__ __forceinline__ const BlobHdr* blob_hdr(const uint8_t* b) {
   return reinterpret_cast<const BlobHdr*>(b);
 }
 __device__ __forceinline__ float blob_step(const uint8_t* b, int g) {
-  return reinterpret_cast<const float*>(b + 64)[g];
+  return uni(reinterpret_cast<const float*>(b + 64)[g]);
 }
 __device__ __forceinline__ const uint8_t* blob_lg(const uint8_t* b, int G) { return b + 64 + 4 * G; }
+__device__ __forceinline__ int layer_group(const uint8_t* b, int G, int l) {
+  return uni((uint32_t)blob_lg(b, G)[l]);
+}
+__device__ __forceinline__ bool blob_ok(const uint8_t* b, int L, int H, int D, int G) {
+  const BlobHdr* bh = reinterpret_cast<const BlobHdr*>(b);
+  return uni(bh->magic) == kTableMagic && uni(bh->version) == kVersion && (int)uni(bh->L) == L &&
+         (int)uni(bh->H) == H && (int)uni(bh->D) == D && (int)uni(bh->G) == G;
+}
+__device__ __forceinline__ bool qflag(const uint8_t* b, int L, int H, int D, int G, int g) {
+  return uni(reinterpret_cast<const uint32_t*>(b + tb_qflag_offset(L, H, D, G))[g]) != 0;
+}
 
 // ---------------------------------------------------------------------------
 // fill / copy / refs
@@ -215,24 +266,60 @@ __global__ void k_qcheck(QCheckArgs a) {
   const float step = blob_step(a.blob, g);
   const float rcp = 1.0f / step;
   uint32_t s0 = 0, n0 = 0;
-  const int32_t qf = quantize<false>((uint16_t)xh, step, rcp, true, s0, n0);
-  const int32_t qi = quantize<false>((uint16_t)xh, step, rcp, false, s0, n0);
+  const int32_t qf = quantize<true>((uint16_t)xh, step, rcp, s0, n0);
+  const int32_t qi = quantize<false>((uint16_t)xh, step, rcp, s0, n0);
   if (qf != qi) atomicAnd(&a.qflags[g], 0u);
 }
 
 // ---------------------------------------------------------------------------
 // histogram: one workgroup per (layer, K|V, head, slice); 8 wavefronts split
-// the tokens; counts privatised in LDS (64 channels x 256 symbols, padded
-// stride so lanes with equal symbols hit different banks).
+// the tokens (a wavefront starting inside a chunk re-quantizes the token
+// before its range). Counts are privatised in LDS lane-minor, hist[sym][lane],
+// so the 64 lanes of an increment hit 64 different banks; row 256 takes the
+// first token of each chunk (no symbol). Counts land in HBM in the same
+// lane-minor order per table set, so the flush is coalesced.
 // ---------------------------------------------------------------------------
 constexpr int kHistThreads = 512;
 constexpr int kHistWaves = kHistThreads / 64;
-constexpr int kHistBatch = 8;
+constexpr int kHistBatch = 16;
+
+template <bool FAST>
+__device__ __forceinline__ void hist_range(const uint16_t* __restrict__ xb, int64_t t_begin,
+                                           int64_t t_end, int C, int D, float step, float rcp,
+                                           uint32_t* hist, int lane, uint32_t& elems,
+                                           uint32_t& sat, uint32_t& nan_, uint32_t& esc) {
+  int32_t prev = 0;
+  int pos = (int)(t_begin % C);  // position of t_begin inside its chunk
+  if (pos != 0) {
+    uint32_t d0 = 0, d1 = 0;
+    prev = quantize<FAST>(xb[(size_t)(t_begin - 1) * D], step, rcp, d0, d1);
+  }
+  for (int64_t t = t_begin; t < t_end; t += kHistBatch) {
+    uint16_t xv[kHistBatch];
+#pragma unroll
+    for (int k = 0; k < kHistBatch; ++k) {
+      const int64_t tk = t + k < t_end ? t + k : t_end - 1;
+      xv[k] = xb[(size_t)tk * D];
+    }
+#pragma unroll
+    for (int k = 0; k < kHistBatch; ++k) {
+      if (t + k < t_end) {
+        const int32_t q = quantize<FAST>(xv[k], step, rcp, sat, nan_);
+        const uint32_t sym = pos != 0 ? symbol_of(wrap16(q - prev)) : 256u;
+        atomicAdd(&hist[sym * 64 + lane], 1u);
+        esc += (sym == (uint32_t)kEsc);
+        prev = q;
+        pos = (pos + 1 == C) ? 0 : pos + 1;
+      }
+    }
+  }
+  elems += (uint32_t)(t_end - t_begin);
+}
 
 __global__ void __launch_bounds__(kHistThreads) k_hist(HistArgs a) {
-  __shared__ uint32_t hist[kLanes * kEncLdsStride];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  for (int i = tid; i < kLanes * kEncLdsStride; i += kHistThreads) hist[i] = 0;
+  __shared__ uint32_t hist[257 * 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  for (int i = tid; i < 257 * 64; i += kHistThreads) hist[i] = 0;
 
   const Shape s = a.s;
   int64_t bid = blockIdx.x;
@@ -243,48 +330,27 @@ __global__ void __launch_bounds__(kHistThreads) k_hist(HistArgs a) {
   const int kv = (int)(bid % 2);
   const int l = (int)(bid / 2);
   const int G = a.G;
-  const int g = blob_lg(a.blob, G)[l];
+  const int g = layer_group(a.blob, G, l);
   const float step = blob_step(a.blob, g);
   const float rcp = 1.0f / step;
-  const uint32_t* qflags = reinterpret_cast<const uint32_t*>(a.blob + tb_qflag_offset(s.L, s.H, s.D, G));
-  const bool fast = qflags[g] != 0;
+  const bool fast = qflag(a.blob, s.L, s.H, s.D, G, g);
   __syncthreads();
 
   const uint16_t* __restrict__ xb =
       a.x + (((size_t)l * 2 + kv) * s.H + h) * (size_t)s.T * s.D + 64 * j + lane;
   const int64_t t_begin = s.T * wave / kHistWaves, t_end = s.T * (wave + 1) / kHistWaves;
-  uint32_t* my = hist + lane * kEncLdsStride;
   uint32_t sat = 0, nan_ = 0, esc = 0, elems = 0;
-  int32_t prev = 0;
-  int64_t pos = t_begin % s.C;  // position inside the chunk
-  if (t_begin < t_end && pos != 0) {
-    uint32_t d0 = 0, d1 = 0;
-    prev = quantize<false>(xb[(size_t)(t_begin - 1) * s.D], step, rcp, fast, d0, d1);
-  }
-  for (int64_t t = t_begin; t < t_end; t += kHistBatch) {
-    uint16_t xv[kHistBatch];
-#pragma unroll
-    for (int k = 0; k < kHistBatch; ++k)
-      xv[k] = (t + k < t_end) ? xb[(size_t)(t + k) * s.D] : (uint16_t)0;
-#pragma unroll
-    for (int k = 0; k < kHistBatch; ++k) {
-      if (t + k < t_end) {
-        const int32_t q = quantize<true>(xv[k], step, rcp, fast, sat, nan_);
-        elems += 1;
-        if (pos != 0) {
-          const uint32_t sym = symbol_of(wrap16(q - prev));
-          atomicAdd(&my[sym], 1u);
-          esc += (sym == (uint32_t)kEsc);
-        }
-        prev = q;
-        pos = (pos + 1 == s.C) ? 0 : pos + 1;
-      }
-    }
+  if (t_begin < t_end) {
+    if (fast)
+      hist_range<true>(xb, t_begin, t_end, s.C, s.D, step, rcp, hist, lane, elems, sat, nan_, esc);
+    else
+      hist_range<false>(xb, t_begin, t_end, s.C, s.D, step, rcp, hist, lane, elems, sat, nan_, esc);
   }
   __syncthreads();
-  uint32_t* counts = a.counts + ((((size_t)g * 2 + kv) * s.H + h) * s.D + 64 * j) * 256;
-  for (int i = tid; i < kLanes * 256; i += kHistThreads) {
-    const uint32_t c = hist[(i >> 8) * kEncLdsStride + (i & 255)];
+  const size_t set = (((size_t)g * 2 + kv) * s.H + h) * s.S + j;
+  uint32_t* counts = a.counts + set * (256 * 64);
+  for (int i = tid; i < 256 * 64; i += kHistThreads) {
+    const uint32_t c = hist[i];
     if (c) atomicAdd(&counts[i], c);
   }
   if (a.stats) {
@@ -314,12 +380,13 @@ __global__ void __launch_bounds__(kNormThreads) k_norm(NormArgs a) {
   for (int i = lane; i < 128; i += 64) bm_lds[wave][i] = 0;
   uint32_t c[4] = {0, 0, 0, 0}, f[4] = {0, 0, 0, 0}, b[4] = {0, 0, 0, 0};
   uint32_t rank0 = 0, K = 0;
+  // table t is channel kk of set t / 64 (sets are lane-minor, 64 channels)
+  const int64_t set = t >> 6;
+  const int kk = (int)(t & 63);
   if (active) {
-    const uint4 cv = reinterpret_cast<const uint4*>(a.counts + t * 256)[lane];
-    c[0] = cv.x;
-    c[1] = cv.y;
-    c[2] = cv.z;
-    c[3] = cv.w;
+    const uint32_t* cs = a.counts + set * (256 * 64) + kk;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[k] = cs[(4 * lane + k) * 64];
     const uint64_t n = wave_sum((uint64_t)c[0] + c[1] + c[2] + c[3]);
     if (n == 0) {
       if (lane == 127 / 4) f[127 % 4] = kM;
@@ -381,46 +448,111 @@ __global__ void __launch_bounds__(kNormThreads) k_norm(NormArgs a) {
   fv.x = f[0] | (f[1] << 16);
   fv.y = f[2] | (f[3] << 16);
   reinterpret_cast<uint2*>(fsec)[lane] = fv;
-  // encoder table: f | b << 16 per symbol
-  uint4 ev;
-  ev.x = f[0] | (b[0] << 16);
-  ev.y = f[1] | (b[1] << 16);
-  ev.z = f[2] | (b[2] << 16);
-  ev.w = f[3] | (b[3] << 16);
-  reinterpret_cast<uint4*>(a.blob + a.enc_off)[t * 64 + lane] = ev;
-  // decoder table: bitmap of symbol starts, rank bases, rank -> (sym, f-1, b)
-  uint32_t* dec = reinterpret_cast<uint32_t*>(a.blob + a.dec_off) + t * kDecDwords;
+  // encoder set: f | b << 16 per symbol
+  uint32_t* enc = reinterpret_cast<uint32_t*>(a.blob + a.enc_off) + set * (kEncDwords * 64) + kk;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) enc[(4 * lane + k) * 64] = f[k] | (b[k] << 16);
+  // decoder set: reversed start bitmap, scaled rank bases, rank -> (d, 4096-f, b)
+  uint32_t* dec = reinterpret_cast<uint32_t*>(a.blob + a.dec_off) + set * (kDecDwords * 64) + kk;
   const uint32_t w0 = bm_lds[wave][2 * lane], w1 = bm_lds[wave][2 * lane + 1];
   const uint32_t p0 = __popc(w0), p1 = __popc(w1);
-  const uint32_t pex = wave_excl_scan(p0 + p1, lane);
-  dec[2 * lane] = w0;
-  dec[2 * lane + 1] = w1;
-  dec[128 + 2 * lane] = pex - 1u;
-  dec[128 + 2 * lane + 1] = pex + p0 - 1u;
+  const uint32_t pex = wave_excl_scan(p0 + p1, lane);  // starts below word 2*lane
+  const uint32_t info_col = 4u * kDecInfo + 4u * (uint32_t)kk;
+  dec[kDecBm + (2 * lane) * 64] = __builtin_bitreverse32(w0) << 1;
+  dec[kDecBm + (2 * lane + 1) * 64] = __builtin_bitreverse32(w1) << 1;
+  dec[kDecRb + (2 * lane) * 64] = ((pex + p0 - 1u) << 8) + info_col;
+  dec[kDecRb + (2 * lane + 1) * 64] = ((pex + p0 + p1 - 1u) << 8) + info_col;
   uint32_t r = rank0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     if (f[k]) {
-      dec[256 + r] = (uint32_t)(4 * lane + k) | ((f[k] - 1u) << 8) | (b[k] << 20);
+      const uint32_t dbyte = (uint32_t)(4 * lane + k - 127) & 255u;
+      dec[kDecInfo + r * 64] = dbyte | ((kM - f[k]) << 8) | (b[k] << 20);
       r += 1;
     }
-    if ((uint32_t)(4 * lane + k) >= K) dec[256 + 4 * lane + k] = 0;
+    if ((uint32_t)(4 * lane + k) >= K) dec[kDecInfo + (4 * lane + k) * 64] = 0;
   }
 }
 
 // ---------------------------------------------------------------------------
 // encode: one workgroup per (chunk, layer group, K|V, head, slice); its 16
-// wavefronts take the layers of the group; the group's 64 encoder tables and
-// a table of RU(1/f) for f = 1..4096 sit in LDS.
-// Exact quotient: floor(x/f) = trunc(fl64(x) * RU(1/f)) for x < 2^32, f <= 2^12.
+// wavefronts take the layers of the group. The set's encoder table (lane-
+// minor, 64 KB) and RU(1/f) for f = 1..4096 (32 KB) sit in LDS.
+// Exact quotient: floor(x/f) = trunc(fl64(x) * RU(1/f)) for x < 2^32, f <= 2^12
+// (the product stays below q+1 by more than the fp64 spacing there).
+// The group is coded backward (token n-1 first) and its words are written
+// backward into a worst-case scratch slot: per token first the escape
+// payloads, then the renormalisation words, so that the decoder, reading
+// forward, meets renorm words before escape payloads.
 // ---------------------------------------------------------------------------
 constexpr int kEncThreads = kWaves * 64;
-constexpr int kEncBatch = 8;
+constexpr int kEncBatch = 16;
+
+template <bool FAST>
+__device__ __forceinline__ void encode_group(const uint16_t* __restrict__ xb, int64_t n, int D,
+                                             float step, float rcp, const uint32_t* ftab,
+                                             const double* rcp_tab, uint16_t* __restrict__ sb,
+                                             uint32_t cap, int lane, uint32_t& words,
+                                             uint32_t& start, bool& table_err) {
+  uint32_t P = cap;
+  uint32_t x = kL;
+  uint32_t d0 = 0, d1 = 0;
+  int32_t qhi = quantize<FAST>(xb[(size_t)(n - 1) * D], step, rcp, d0, d1);
+  bool terr = false;
+  for (int64_t i = n - 1; i >= 1; i -= kEncBatch) {
+    uint16_t xv[kEncBatch];
+#pragma unroll
+    for (int k = 0; k < kEncBatch; ++k) {
+      const int64_t row = i - 1 - k >= 0 ? i - 1 - k : 0;
+      xv[k] = xb[(size_t)row * D];
+    }
+#pragma unroll
+    for (int k = 0; k < kEncBatch; ++k) {
+      if (i - k >= 1) {
+        const int32_t qlo = quantize<FAST>(xv[k], step, rcp, d0, d1);
+        const int32_t dlt = wrap16(qhi - qlo);
+        const uint32_t sym = symbol_of(dlt);
+        const uint32_t e = ftab[sym * 64 + lane];
+        const uint32_t f = e & 0xFFFFu, bb = e >> 16;
+        terr |= (f == 0);
+        const bool is_esc = sym == (uint32_t)kEsc;
+        const uint64_t me = __ballot(is_esc);
+        if (me) {
+          P -= (uint32_t)__popcll(me);
+          if (is_esc) sb[mbcnt_base(me, P)] = (uint16_t)(dlt & 0xFFFF);
+        }
+        // renormalise when x >= f * 2^20, i.e. x > (f << 20) - 1 (wraps to ~0 for f = 4096)
+        const bool need = x > ((f << 20) - 1u);
+        const uint64_t mr = __ballot(need);
+        P -= (uint32_t)__popcll(mr);
+        if (need) {
+          sb[mbcnt_base(mr, P)] = (uint16_t)(x & 0xFFFFu);
+          x >>= 16;
+        }
+        // x <- floor(x/f)*4096 + x mod f + b = x + floor(x/f)*(4096-f) + b
+        // (f = 0 only for a symbol missing from the table: the group is then
+        // invalid and CG_ERR_TABLE is reported; rcp_tab[0] = 0 keeps it finite)
+        const uint32_t qd = (uint32_t)((double)x * rcp_tab[f]);
+        x = x + qd * (kM - f) + bb;
+        qhi = qlo;
+      }
+    }
+  }
+  P -= 64;
+  sb[P + lane] = (uint16_t)(qhi & 0xFFFF);
+  P -= 64;
+  sb[P + lane] = (uint16_t)(x & 0xFFFFu);
+  P -= 64;
+  sb[P + lane] = (uint16_t)(x >> 16);
+  words = cap - P;
+  start = P;
+  table_err |= terr;
+}
 
 __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
-  __shared__ uint32_t ftab[kLanes * kEncLdsStride];
+  __shared__ uint32_t ftab[kEncDwords * 64];
   __shared__ double rcp_tab[kM + 1];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const Shape s = a.s;
   int64_t bid = blockIdx.x;
   const int j = (int)(bid % s.S);
@@ -433,23 +565,14 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
   const int64_t cl = bid / a.G;  // chunk index within the call
   const int64_t c = a.chunk_begin + cl;
   const int G = a.G;
-  const BlobHdr* bh = blob_hdr(a.blob);
-  if (bh->magic != kTableMagic || bh->version != kVersion || (int)bh->L != s.L ||
-      (int)bh->H != s.H || (int)bh->D != s.D || (int)bh->G != G) {
+  if (!blob_ok(a.blob, s.L, s.H, s.D, G)) {
     if (tid == 0) set_status(a.status, CG_ERR_INVALID_ARG);
     return;
   }
-  const uint64_t enc_off = tb_enc_offset(s.L, s.H, s.D, G);
-  const uint32_t* esrc = reinterpret_cast<const uint32_t*>(a.blob + enc_off) +
-                         ((((size_t)g * 2 + kv) * s.H + h) * s.D + 64 * j) * kEncDwords;
-  for (int u = tid; u < kLanes * kEncDwords / 4; u += kEncThreads) {
-    const uint4 v = reinterpret_cast<const uint4*>(esrc)[u];
-    uint32_t* d = ftab + (u >> 6) * kEncLdsStride + (u & 63) * 4;
-    d[0] = v.x;
-    d[1] = v.y;
-    d[2] = v.z;
-    d[3] = v.w;
-  }
+  const size_t set = (((size_t)g * 2 + kv) * s.H + h) * s.S + j;
+  const uint4* esrc = reinterpret_cast<const uint4*>(
+      reinterpret_cast<const uint32_t*>(a.blob + tb_enc_offset(s.L, s.H, s.D, G)) + set * (kEncDwords * 64));
+  for (int u = tid; u < kEncDwords * 64 / 4; u += kEncThreads) reinterpret_cast<uint4*>(ftab)[u] = esrc[u];
   for (int f = tid + 1; f <= (int)kM; f += kEncThreads) {
     double r = 1.0 / (double)f;
     if (__builtin_fma(r, (double)f, -1.0) < 0.0) r = __longlong_as_double(__double_as_longlong(r) + 1);
@@ -460,75 +583,28 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
 
   const float step = blob_step(a.blob, g);
   const float rcp = 1.0f / step;
-  const uint32_t* qflags = reinterpret_cast<const uint32_t*>(a.blob + tb_qflag_offset(s.L, s.H, s.D, G));
-  const bool fast = qflags[g] != 0;
-  const uint8_t* lg = blob_lg(a.blob, G);
+  const bool fast = qflag(a.blob, s.L, s.H, s.D, G, g);
   const int64_t n = chunk_len(s.T, s.C, c), t0 = c * s.C;
   const int64_t gpc = groups_per_chunk(s.L, s.H, s.D);
-  const uint32_t* my = ftab + lane * kEncLdsStride;
+  const uint32_t cap = (uint32_t)a.cap_words;
   bool table_err = false;
   int cnt = 0;
   for (int l = 0; l < s.L; ++l) {
-    if (lg[l] != g) continue;
+    if (layer_group(a.blob, G, l) != g) continue;
     if ((cnt++ % kWaves) != wave) continue;
     const int64_t gi = (((int64_t)l * 2 + kv) * s.H + h) * s.S + j;
     const int64_t slot = cl * gpc + gi;
     uint16_t* __restrict__ sb = a.scratch + (size_t)slot * a.cap_words;
     const uint16_t* __restrict__ xb =
         a.x + ((((size_t)l * 2 + kv) * s.H + h) * (size_t)s.T + t0) * s.D + 64 * j + lane;
-    uint32_t P = (uint32_t)a.cap_words;
-    uint32_t x = kL;
-    uint32_t d0 = 0, d1 = 0;
-    int32_t qhi = quantize<false>(xb[(size_t)(n - 1) * s.D], step, rcp, fast, d0, d1);
-    for (int64_t i = n - 1; i >= 1; i -= kEncBatch) {
-      uint16_t xv[kEncBatch];
-#pragma unroll
-      for (int k = 0; k < kEncBatch; ++k)
-        xv[k] = (i - 1 - k >= 0) ? xb[(size_t)(i - 1 - k) * s.D] : (uint16_t)0;
-#pragma unroll
-      for (int k = 0; k < kEncBatch; ++k) {
-        if (i - k >= 1) {
-          const int32_t qlo = quantize<false>(xv[k], step, rcp, fast, d0, d1);
-          const int32_t dlt = wrap16(qhi - qlo);
-          const uint32_t sym = symbol_of(dlt);
-          const uint32_t e = my[sym];
-          uint32_t f = e & 0xFFFFu, bb = e >> 16;
-          if (f == 0) {
-            table_err = true;
-            f = kM;
-            bb = 0;
-          }
-          // escape payloads of this token (read after its renorm words)
-          const bool is_esc = sym == (uint32_t)kEsc;
-          const uint64_t me = __ballot(is_esc);
-          if (me) {
-            P -= (uint32_t)__popcll(me);
-            if (is_esc) sb[P + mbcnt(me)] = (uint16_t)(dlt & 0xFFFF);
-          }
-          // renormalise: x >= f * 2^20  <=>  x > (f << 20) - 1 (wraps to ~0 for f = 4096)
-          const bool need = x > ((f << 20) - 1u);
-          const uint64_t mr = __ballot(need);
-          P -= (uint32_t)__popcll(mr);
-          if (need) {
-            sb[P + mbcnt(mr)] = (uint16_t)(x & 0xFFFFu);
-            x >>= 16;
-          }
-          // x <- floor(x/f)*4096 + x mod f + b  =  x + floor(x/f)*(4096-f) + b
-          const uint32_t qd = (uint32_t)((double)x * rcp_tab[f]);
-          x = x + qd * (kM - f) + bb;
-          qhi = qlo;
-        }
-      }
-    }
-    P -= 64;
-    sb[P + lane] = (uint16_t)(qhi & 0xFFFF);
-    P -= 64;
-    sb[P + lane] = (uint16_t)(x & 0xFFFFu);
-    P -= 64;
-    sb[P + lane] = (uint16_t)(x >> 16);
+    uint32_t words, start;
+    if (fast)
+      encode_group<true>(xb, n, s.D, step, rcp, ftab, rcp_tab, sb, cap, lane, words, start, table_err);
+    else
+      encode_group<false>(xb, n, s.D, step, rcp, ftab, rcp_tab, sb, cap, lane, words, start, table_err);
     if (lane == 0) {
-      a.group_words[slot] = (uint32_t)a.cap_words - P;
-      a.group_start[slot] = P;
+      a.group_words[slot] = words;
+      a.group_start[slot] = start;
     }
   }
   if (__ballot(table_err) && lane == 0) set_status(a.status, CG_ERR_TABLE);
@@ -601,15 +677,15 @@ __global__ void __launch_bounds__(kScanThreads) k_chunk_scan(ChunkScanArgs a) {
 constexpr int kWriteThreads = 256;
 
 __global__ void __launch_bounds__(kWriteThreads) k_write(WriteArgs a) {
-  if (a.chunk_offsets[a.n_chunks] > a.out_cap) return;
+  if (uni(a.chunk_offsets[a.n_chunks]) > a.out_cap) return;
   const int64_t nblk = 1 + (a.gpc + a.groups_per_block - 1) / a.groups_per_block;
   const int64_t cl = blockIdx.x / nblk, blk = blockIdx.x % nblk;
   const int64_t c = a.chunk_begin + cl;
-  uint8_t* rec = a.out + a.chunk_offsets[cl];
+  uint8_t* rec = a.out + uni(a.chunk_offsets[cl]);
   const uint64_t ds = rec_data_start(a.gpc);
   const uint64_t* go = a.group_off + cl * (a.gpc + 1);
-  const uint64_t data_bytes = go[a.gpc];
-  const uint64_t rbytes = a.rec_bytes[cl];
+  const uint64_t data_bytes = uni(go[a.gpc]);
+  const uint64_t rbytes = uni(a.rec_bytes[cl]);
   const int tid = threadIdx.x;
   if (blk == 0) {
     const uint64_t tab_end = 64 + 8 * (uint64_t)(a.gpc + 1) + 4 * (uint64_t)a.gpc;
@@ -637,38 +713,74 @@ __global__ void __launch_bounds__(kWriteThreads) k_write(WriteArgs a) {
     }
     return;
   }
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = wave_id(), lane = tid & 63;
   const int64_t g_begin = (blk - 1) * a.groups_per_block;
   for (int64_t gi = g_begin + wave; gi < g_begin + a.groups_per_block && gi < a.gpc;
        gi += kWriteThreads / 64) {
     const int64_t slot = cl * a.gpc + gi;
-    const uint32_t nw = a.group_words[slot];
-    const uint16_t* src = a.scratch + (size_t)slot * a.cap_words + a.group_start[slot];
-    uint32_t* dst = reinterpret_cast<uint32_t*>(rec + ds + go[gi]);
-    const uint32_t ndw = (uint32_t)((go[gi + 1] - go[gi]) / 4);
-    for (uint32_t k = lane; k < ndw; k += 64) {
-      const uint32_t w0 = 2 * k < nw ? src[2 * k] : 0u;
-      const uint32_t w1 = 2 * k + 1 < nw ? src[2 * k + 1] : 0u;
-      dst[k] = w0 | (w1 << 16);
+    const uint32_t nw = uni(a.group_words[slot]);
+    const uint32_t P = uni(a.group_start[slot]);
+    // the slot is 16-byte aligned; the stream is words [P, P + nw) of it
+    const uint32_t* __restrict__ s32 =
+        reinterpret_cast<const uint32_t*>(a.scratch + (size_t)slot * a.cap_words);
+    const uint64_t g0 = uni(go[gi]), g1 = uni(go[gi + 1]);
+    uint32_t* __restrict__ dst = reinterpret_cast<uint32_t*>(rec + ds + g0);
+    const uint32_t ndw = (uint32_t)((g1 - g0) / 4);
+    const uint32_t base = P >> 1;
+    if ((P & 1) == 0) {
+      for (uint32_t k = lane; k < ndw; k += 64) {
+        uint32_t w = 0;
+        if (2 * k + 1 < nw) {
+          w = s32[base + k];
+        } else if (2 * k < nw) {
+          w = s32[base + k] & 0xFFFFu;
+        }
+        dst[k] = w;
+      }
+    } else {
+      // word 2k of the stream is the high half of dword base+k
+      for (uint32_t k = lane; k < ndw; k += 64) {
+        uint32_t w = 0;
+        if (2 * k < nw) w = s32[base + k] >> 16;
+        if (2 * k + 1 < nw) w |= s32[base + k + 1] << 16;
+        dst[k] = w;
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// decode: one workgroup per (record, layer group, K|V, head, slice); the 64
-// decoder tables of the slice sit in LDS and each wavefront decodes the
-// groups of one layer at a time. Per wavefront a 512-word LDS ring holds the
-// stream, refilled 256 words ahead with coalesced 8-byte loads.
+// decode: one workgroup per (record, layer group, K|V, head, slice); the
+// set's decoder tables (lane-minor, 128 KB) sit in LDS and each wavefront
+// decodes the group of one layer at a time. Per wavefront a 512-word LDS ring
+// (+ 64-word mirror) holds the stream, refilled 256 words ahead with
+// coalesced 8-byte loads.
 //
-// Per token and lane: slot = x & 4095; rank = rankbase[slot>>5] +
-// popcount(bitmap[slot>>5] << (31 - (slot&31))); (sym, f, b) = info[rank];
-// x = f*(x>>12) + slot - b; renormalise from the ring (ballot + mbcnt);
-// escape payload likewise; q += d (mod 2^16); y = fp16(fl32(q*step)).
+// Per token and lane (x = rANS state, slot = x & 4095):
+//   w = slot >> 5; rank = rankbase[w] + popcount(bitmap[w] << (31 - (slot & 31)))
+//   info = sym | (4096 - f) << 8 | b << 20
+//   x = x - ((4096 - f) * (x >> 12) + b)      (= f * (x >> 12) + slot - b)
+//   x < 2^16: x = x << 16 | next renorm word (ballot + mbcnt)
+//   sym 255: d = next escape payload, else d = sym - 127
+//   q = q + d (mod 2^16); y = fp16(fl32(q * step))
 // ---------------------------------------------------------------------------
 constexpr int kDecThreads = kWaves * 64;
+constexpr int kRingStride = kRingWords + kRingMirror;  // 16-bit words per wavefront
+
+// a * b + c on 24-bit signed operands in one instruction (the compiler would
+// split a multiply by -256 into a shift and a subtraction)
+__device__ __forceinline__ uint32_t mad_i24(uint32_t a, int32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_mad_i32_i24 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(b), "v"(c));
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const uint32_t* base, uint32_t byte_off) {
+  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(base) + byte_off);
+}
 
 template <bool PAGED>
-__device__ __forceinline__ void decode_group(const DecodeArgs& a, const uint32_t* __restrict__ tabs,
+__device__ __forceinline__ void decode_group(const DecodeArgs& a, const uint32_t* tabs,
                                              uint16_t* ring, const uint8_t* __restrict__ rec,
                                              uint64_t ds, uint64_t data_bytes, int64_t gpc, int l,
                                              int kv, int h, int j, int64_t t0, int64_t n,
@@ -677,22 +789,26 @@ __device__ __forceinline__ void decode_group(const DecodeArgs& a, const uint32_t
   const int64_t gi = (((int64_t)l * 2 + kv) * s.H + h) * s.S + j;
   const uint64_t* goffs = reinterpret_cast<const uint64_t*>(rec + 64);
   const uint32_t* gwords = reinterpret_cast<const uint32_t*>(rec + 64 + 8 * (gpc + 1));
-  const uint64_t o0 = goffs[gi], o1 = goffs[gi + 1];
-  const uint32_t nw = gwords[gi];
+  const uint64_t o0 = uni(goffs[gi]), o1 = uni(goffs[gi + 1]);
+  const uint32_t nw = uni(gwords[gi]);
   if ((o0 & 15) || (o1 & 15) || o0 > o1 || o1 > data_bytes || 2ull * nw > o1 - o0 ||
-      nw < (uint32_t)kHdrWords || (gi == 0 && o0 != 0) || (gi == gpc - 1 && o1 != data_bytes)) {
+      nw < (uint32_t)kHdrWords || (o1 - o0) >= (1ull << 32) || (gi == 0 && o0 != 0) ||
+      (gi == gpc - 1 && o1 != data_bytes)) {
     if (lane == 0) set_status(a.status, CG_ERR_CORRUPT);
     return;
   }
-  const uint8_t* __restrict__ gb = rec + ds + o0;
-  const uint32_t pw = (uint32_t)((o1 - o0) >> 1);  // readable words, multiple of 8
+  // the group's stream: words past its padded end read as 0
+  const __amdgpu_buffer_rsrc_t src = make_rsrc(rec + ds + o0, (uint32_t)(o1 - o0));
+  const uint32_t lane8 = 8u * lane;
   auto load4 = [&](uint32_t wbase) -> uint2 {
-    const uint32_t w = wbase + 4u * lane;
-    if (w + 4u <= pw) return *reinterpret_cast<const uint2*>(gb + 2ull * w);
-    return make_uint2(0u, 0u);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(src, lane8, 2 * wbase, 0);
+    return make_uint2(v[0], v[1]);
   };
+  // words [wbase, wbase+256) -> ring; block 0 also refreshes the mirror of words 0..63
   auto put4 = [&](uint32_t wbase, uint2 v) {
-    *reinterpret_cast<uint2*>(ring + ((wbase + 4u * lane) & (kRingWords - 1))) = v;
+    const uint32_t r = (wbase + 4u * lane) & (kRingWords - 1);
+    *reinterpret_cast<uint2*>(ring + r) = v;
+    if (r < (uint32_t)kRingMirror) *reinterpret_cast<uint2*>(ring + kRingWords + r) = v;
   };
   {
     const uint2 v0 = load4(0), v1 = load4(256);
@@ -704,57 +820,63 @@ __device__ __forceinline__ void decode_group(const DecodeArgs& a, const uint32_t
   __builtin_amdgcn_wave_barrier();
 
   uint32_t x = ((uint32_t)ring[lane] << 16) | ring[64 + lane];
-  int32_t q = (int16_t)ring[128 + lane];
+  uint32_t q = ring[128 + lane];  // q modulo 2^16 lives in the low half
   uint32_t p = kHdrWords;
-  const uint32_t* __restrict__ tb = tabs + lane * kDecLdsStride;
+  const uint32_t lane4 = 4u * lane;
+  constexpr uint32_t kRbOff = 4u * (kDecRb - kDecBm);
 
-  uint16_t* __restrict__ yp = nullptr;
-  size_t ystride = 0;
+  // destination rows: contiguous y[l][kv][h][t][64j ..] or pool[l][kv][blk][h][t%16][64j ..]
+  const uint32_t lane2 = 2u * lane;
+  const uint32_t row_bytes = 2u * (uint32_t)s.D;
+  __amdgpu_buffer_rsrc_t dst;
+  uint32_t doff = 0;
+  const size_t col = (size_t)64 * j;
   if (!PAGED) {
-    yp = a.y + ((((size_t)l * 2 + kv) * s.H + h) * (size_t)s.T + t0) * s.D + 64 * j + lane;
-    ystride = (size_t)s.D;
-    yp[0] = dequantize(q, step);
+    const uint16_t* y0 = a.y + ((((size_t)l * 2 + kv) * s.H + h) * (size_t)s.T + t0) * s.D + col;
+    dst = make_rsrc(y0, (uint32_t)(n * row_bytes));
+  } else {
+    const uint16_t* p0 = a.pool + ((size_t)l * 2 + kv) * (size_t)a.num_blocks * s.H * 16 * s.D + col;
+    dst = make_rsrc(p0, (uint32_t)((uint64_t)a.num_blocks * s.H * 16 * row_bytes));
   }
-  const size_t pool_base = PAGED ? (((size_t)l * 2 + kv) * (size_t)a.num_blocks) : 0;
-  auto pool_ptr = [&](int64_t t) -> uint16_t* {
-    const int32_t blk = __builtin_amdgcn_readfirstlane(a.block_table[t >> 4]);
-    return a.pool + (((pool_base + (size_t)blk) * s.H + h) * 16 + (size_t)(t & 15)) * s.D + 64 * j + lane;
+  auto pool_off = [&](int64_t t) -> uint32_t {
+    const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane(a.block_table[t >> 4]);
+    return ((blk * (uint32_t)s.H + (uint32_t)h) * 16u + (uint32_t)(t & 15)) * row_bytes;
   };
-  if (PAGED) *pool_ptr(t0) = dequantize(q, step);
+  if (PAGED) doff = pool_off(t0);
+  __builtin_amdgcn_raw_buffer_store_b16(dequantize_low16(q, step), dst, lane2, doff, 0);
 
-  for (int64_t i = 1; i < n; ++i) {
+  for (int i = 1; i < (int)n; ++i) {
     if (loaded - p < 256u) {
       put4(loaded, pref);
       loaded += 256;
       pref = load4(loaded);
       __builtin_amdgcn_wave_barrier();
     }
-    const uint32_t slot = x & (kM - 1);
-    const uint32_t wi = slot >> 5;
-    const uint32_t bm = tb[wi], rb = tb[128 + wi];
-    const uint32_t rank = (uint32_t)__popc(bm << (31u - (slot & 31u))) + rb;
-    const uint32_t info = tb[256 + (rank & 255u)];
-    const uint32_t sym = info & 255u, fm1 = (info >> 8) & 4095u, bsym = info >> 20;
-    x = (fm1 + 1u) * (x >> 12) + slot - bsym;
+    // slot -> (d, 4096 - f, b)
+    const uint32_t ob = ((x << 3) & 0x7F00u) | lane4;  // word (slot >> 5) of this lane
+    const uint32_t above = lds_u32(tabs, ob), rankx = lds_u32(tabs, ob + kRbOff);
+    const uint32_t after = (uint32_t)__popc(above << (x & 31u));  // starts after the slot
+    const uint32_t info = lds_u32(tabs, mad_i24(after, -256, rankx));
+    const uint32_t fp = (info >> 8) & 0xFFFu, bs = info >> 20;
+    x = x - (fp * (x >> 12) + bs);
+    // renormalise
     const bool need = x < kL;
     const uint64_t mr = __ballot(need);
-    if (need) x = (x << 16) | ring[(p + mbcnt(mr)) & (kRingWords - 1)];
+    const uint16_t* rp = ring + (p & (kRingWords - 1));
+    if (need) x = (x << 16) | rp[mbcnt_base(mr, 0)];
     p += (uint32_t)__popcll(mr);
-    int32_t d = (int32_t)sym - 127;
-    const bool is_esc = sym == (uint32_t)kEsc;
+    // token prefix: q += d, or the escape payload (the byte 0x80 added -128)
+    q += (uint32_t)(int32_t)(int8_t)(info & 0xFFu);
+    const bool is_esc = (info & 0xFFu) == 0x80u;
     const uint64_t me = __ballot(is_esc);
     if (me) {
-      if (is_esc) d = (int16_t)ring[(p + mbcnt(me)) & (kRingWords - 1)];
+      const uint16_t* ep = ring + (p & (kRingWords - 1));
+      if (is_esc) q += 128u + ep[mbcnt_base(me, 0)];  // payload = difference mod 2^16
       p += (uint32_t)__popcll(me);
     }
-    q = (int32_t)(int16_t)(q + d);
-    const uint16_t y = dequantize(q, step);
-    if (PAGED) {
-      *pool_ptr(t0 + i) = y;
-    } else {
-      yp += ystride;
-      *yp = y;
-    }
+    const uint16_t y = dequantize_low16(q, step);
+    doff = PAGED ? pool_off(t0 + i) : doff + row_bytes;
+    __builtin_amdgcn_raw_buffer_store_b16(y, dst, lane2, doff, 0);
   }
   const bool bad = (__ballot(x != kL) != 0) || (p != nw);
   if (bad && lane == 0) set_status(a.status, CG_ERR_CORRUPT);
@@ -762,9 +884,9 @@ __device__ __forceinline__ void decode_group(const DecodeArgs& a, const uint32_t
 
 template <bool PAGED>
 __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
-  __shared__ uint32_t tabs[kLanes * kDecLdsStride];
-  __shared__ uint32_t rings[kWaves * kRingWords / 2];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __shared__ uint32_t tabs[kDecDwords * 64];
+  __shared__ uint16_t rings[kWaves * kRingStride];
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const Shape s = a.s;
   int64_t bid = blockIdx.x;
   const int j = (int)(bid % s.S);
@@ -777,8 +899,9 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
   const int64_t r = bid / a.g_max;
   const bool first_block = (g == 0 && kv == 0 && h == 0 && j == 0);
 
-  const cg_chunk_ref ref = a.refs[r];
-  const int ti = ref.table;
+  const uint8_t* rec = uni(a.refs[r].record);
+  const uint64_t ref_bytes = uni(a.refs[r].bytes);
+  const int ti = uni(a.refs[r].table);
   if (ti < 0 || ti >= a.n_tables) {
     if (tid == 0 && first_block) set_status(a.status, CG_ERR_INVALID_ARG);
     return;
@@ -786,33 +909,30 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
   const int G = a.n_groups[ti];
   if (g >= G) return;
   const uint8_t* blob = a.tables[ti];
-  const BlobHdr* bh = blob_hdr(blob);
-  if (bh->magic != kTableMagic || bh->version != kVersion || (int)bh->L != s.L ||
-      (int)bh->H != s.H || (int)bh->D != s.D || (int)bh->G != G ||
-      (int32_t)bh->level_id != a.level_id[ti]) {
+  if (!blob_ok(blob, s.L, s.H, s.D, G) ||
+      (int32_t)uni(blob_hdr(blob)->level_id) != a.level_id[ti]) {
     if (tid == 0) set_status(a.status, CG_ERR_INVALID_ARG);
     return;
   }
   // record header
-  const uint8_t* rec = ref.record;
   const int64_t gpc = groups_per_chunk(s.L, s.H, s.D);
   const uint64_t ds_expect = rec_data_start(gpc);
-  if (ref.bytes < ds_expect || (reinterpret_cast<uintptr_t>(rec) & 15)) {
+  if (ref_bytes < ds_expect || (reinterpret_cast<uintptr_t>(rec) & 15)) {
     if (tid == 0) set_status(a.status, CG_ERR_CORRUPT);
     return;
   }
   const uint32_t* rh = reinterpret_cast<const uint32_t*>(rec);
-  const int64_t c = rh[2];
+  const int64_t c = uni(rh[2]);
   const int64_t nch = n_chunks(s.T, s.C);
-  const uint64_t rbytes = *reinterpret_cast<const uint64_t*>(rec + 48);
-  const uint64_t dbytes = *reinterpret_cast<const uint64_t*>(rec + 56);
-  bool bad = rh[0] != kRecordMagic || rh[1] != kVersion || c >= nch ||
-             (int32_t)rh[3] != a.level_id[ti];
+  const uint64_t rbytes = uni(*reinterpret_cast<const uint64_t*>(rec + 48));
+  const uint64_t dbytes = uni(*reinterpret_cast<const uint64_t*>(rec + 56));
+  bool bad = uni(rh[0]) != kRecordMagic || uni(rh[1]) != kVersion || c >= nch ||
+             (int32_t)uni(rh[3]) != a.level_id[ti];
   if (!bad) {
-    bad = *reinterpret_cast<const uint64_t*>(rec + 16) != (uint64_t)(c * s.C) ||
-          rh[6] != (uint32_t)chunk_len(s.T, s.C, c) || rh[7] != (uint32_t)gpc ||
-          (int)rh[8] != s.L || (int)rh[9] != s.H || (int)rh[10] != s.D || rh[11] != ds_expect ||
-          rbytes > ref.bytes || ds_expect + dbytes > rbytes;
+    bad = uni(*reinterpret_cast<const uint64_t*>(rec + 16)) != (uint64_t)(c * s.C) ||
+          uni(rh[6]) != (uint32_t)chunk_len(s.T, s.C, c) || uni(rh[7]) != (uint32_t)gpc ||
+          (int)uni(rh[8]) != s.L || (int)uni(rh[9]) != s.H || (int)uni(rh[10]) != s.D ||
+          uni(rh[11]) != ds_expect || rbytes > ref_bytes || ds_expect + dbytes > rbytes;
   }
   if (bad) {
     if (tid == 0) set_status(a.status, CG_ERR_CORRUPT);
@@ -830,24 +950,17 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
       return;
     }
   }
-  // the 64 decoder tables of this (group, K|V, head, slice)
-  const uint32_t* dsrc = reinterpret_cast<const uint32_t*>(blob + tb_dec_offset(s.L, s.H, s.D, G)) +
-                         ((((size_t)g * 2 + kv) * s.H + h) * s.D + 64 * j) * kDecDwords;
-  for (int u = tid; u < kLanes * kDecDwords / 4; u += kDecThreads) {
-    const uint4 v = reinterpret_cast<const uint4*>(dsrc)[u];
-    uint32_t* d = tabs + (u >> 7) * kDecLdsStride + (u & 127) * 4;
-    d[0] = v.x;
-    d[1] = v.y;
-    d[2] = v.z;
-    d[3] = v.w;
-  }
+  // the set's decoder tables, one contiguous 128 KB block
+  const size_t set = (((size_t)g * 2 + kv) * s.H + h) * s.S + j;
+  const uint4* dsrc = reinterpret_cast<const uint4*>(
+      reinterpret_cast<const uint32_t*>(blob + tb_dec_offset(s.L, s.H, s.D, G)) + set * (kDecDwords * 64));
+  for (int u = tid; u < kDecDwords * 64 / 4; u += kDecThreads) reinterpret_cast<uint4*>(tabs)[u] = dsrc[u];
   __syncthreads();
   const float step = blob_step(blob, g);
-  const uint8_t* lg = blob_lg(blob, G);
-  uint16_t* ring = reinterpret_cast<uint16_t*>(rings + wave * (kRingWords / 2));
+  uint16_t* ring = rings + wave * kRingStride;
   int cnt = 0;
   for (int l = 0; l < s.L; ++l) {
-    if (lg[l] != g) continue;
+    if (layer_group(blob, G, l) != g) continue;
     if ((cnt++ % kWaves) != wave) continue;
     decode_group<PAGED>(a, tabs, ring, rec, ds_expect, dbytes, gpc, l, kv, h, j, t0, n, step, lane);
   }

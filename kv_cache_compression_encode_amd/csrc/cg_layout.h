@@ -20,15 +20,28 @@ constexpr int kMaxLevels = 8;
 constexpr int kMaxGroups = 255;
 constexpr int kMaxLayers = 1024;
 
-// Decoder table per channel in LDS/HBM: 128 bitmap words, 128 rank bases,
-// 256 rank -> (symbol, f-1, b) entries. 512 dwords; padded to 513 in LDS.
-constexpr int kDecDwords = 512;
-constexpr int kDecLdsStride = 513;
-// Encoder table per channel: 256 dwords (f | b << 16), padded to 257 in LDS.
-constexpr int kEncDwords = 256;
-constexpr int kEncLdsStride = 257;
-// Decoder ring buffer per wavefront: 512 16-bit words, refilled 256 at a time.
+// Lookup tables are stored per "set" = the 64 channels of one (layer group,
+// K|V, head, 64-dim slice), lane-minor: entry e of lane k is dword e*64 + k,
+// so a wavefront reading "its" entries touches 64 different banks and a set
+// is copied to LDS as one contiguous block.
+// Decoder set (128 KB), per 32-slot word w of a lane's slot range:
+//   above[w][64] : bit q (q >= 1) set when a symbol starts at slot 32w + 32 - q
+//                  (the start bitmap reversed and shifted up by one), so
+//                  popcount(above << (slot & 31)) counts starts after the slot;
+//   rankx[w][64] : 256 * (symbols starting at or below slot 32w+31, minus 1)
+//                  + byte address of the lane's info column;
+//   info[256][64]: rank -> d | (4096 - f) << 8 | b << 20 with d = sym - 127 as
+//                  a byte (0x80 = escape).
+// info address = rankx[w] - 256 * popcount(above[w] << (slot & 31)).
+// above and rankx lie in the first 64 KB so one ds_read2st64 fetches both.
+constexpr int kDecDwords = 512;            // per channel
+constexpr int kDecBm = 0, kDecRb = 128 * 64, kDecInfo = 256 * 64;  // dword offsets in a set
+// Encoder set: [256 symbols][64] of f | b << 16. 64 KB.
+constexpr int kEncDwords = 256;            // per channel
+// Decoder ring per wavefront: 512 16-bit words refilled 256 at a time, plus a
+// 64-word mirror of words 0..63 so a read at (p mod 512) + k, k < 64, needs no wrap.
 constexpr int kRingWords = 512;
+constexpr int kRingMirror = 64;
 constexpr int kWaves = 16;  // wavefronts per workgroup of the codec kernels
 
 __host__ __device__ inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
