@@ -18,6 +18,8 @@ def run_level(cd, x, lvd):
     tables = cd.build_tables(x, lv)
     out, offs = cd.encode(x, lv, tables)
     assert cd.read_status() == 0
+    used = int(offs[-1])
+    out = out[:used].clone()  # release the worst-case allocation
     return lv, tables, out, offs
 
 
@@ -105,7 +107,6 @@ def test_stream_paged():
     assert cd.read_status() == 0
     rng = np.random.default_rng(3)
     steps = [lvd.steps[g] for g in lvd.layer_group]
-    inv = np.argsort(bt)  # pool block -> token block
 
     def y_slice(l, kv, h):
         blocks = pool[l, kv, torch.from_numpy(bt.astype(np.int64)).cuda(), h]  # [T/16][16][D]
@@ -114,4 +115,3 @@ def test_stream_paged():
     F.check_slices(cfg, steps, X, y_slice, rng)
     blob = U.u8(tables[:cd.format_bytes(lv)])
     F.check_groups(cfg, X, blob, lambda a, b: U.u8(out[a:b]), offs.cpu().numpy(), rng, n=3)
-    assert len(inv) == NB
