@@ -189,6 +189,24 @@ cg_status cg_decode_paged(const cg_shape* shape, int32_t n_levels, const cg_leve
                           const int32_t* block_table_dev, int32_t* status_dev,
                           const cg_profile* prof, hipStream_t stream);
 
+/* Streaming fill of a paged cache ("CacheGen实战" 2.3: a receive stage, a
+ * parallel GPU decode stage and a fill stage run as a pipeline). Records
+ * [0, n_records) lie in host memory at records_host + offsets_host[k]
+ * (offsets_host has n_records+1 entries; records_host should be pinned, else
+ * the copies are synchronous). Record k is copied host-to-device into one of
+ * two halves of staging_dev on copy_stream while record k-1 is decoded into
+ * pool_dev on stream; table_of_record_host[k] (or 0 when NULL) selects its
+ * level. staging_bytes must hold two copies of the largest record;
+ * refs_dev holds 2 cg_chunk_ref. Returns after enqueueing all work; the last
+ * decode is ordered on stream. Data errors: as cg_decode_paged. */
+cg_status cg_stream_decode_paged(const cg_shape* shape, int32_t n_levels, const cg_level* levels,
+                                 const void* const* tables_dev, const uint8_t* records_host,
+                                 const uint64_t* offsets_host, const int32_t* table_of_record_host,
+                                 int32_t n_records, uint8_t* staging_dev, uint64_t staging_bytes,
+                                 cg_chunk_ref* refs_dev, uint16_t* pool_dev, int64_t num_blocks,
+                                 const int32_t* block_table_dev, int32_t* status_dev,
+                                 hipStream_t stream, hipStream_t copy_stream);
+
 /* ---- measurement helper ---------------------------------------------------- */
 
 /* Plain device copy of `bytes` (a multiple of 16) with the library's launch

@@ -136,6 +136,7 @@ def lib():
         "cg_decode": (i32, [sp, i32, lp, P, P, i32, P, P, pp, P]),
         "cg_decode_paged": (i32, [sp, i32, lp, P, P, i32, P, i64, P, P, pp, P]),
         "cg_copy": (i32, [P, P, u64, P]),
+        "cg_stream_decode_paged": (i32, [sp, i32, lp, P, P, P, P, i32, P, u64, P, P, i64, P, P, P, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(L, name)
@@ -148,7 +149,7 @@ def lib():
 EXPORTS = ("cg_version", "cg_status_string", "cg_tables_bytes", "cg_tables_format_bytes",
            "cg_build_workspace_bytes", "cg_build_tables", "cg_encode_bound",
            "cg_encode_workspace_bytes", "cg_encode", "cg_make_refs", "cg_decode",
-           "cg_decode_paged", "cg_copy")
+           "cg_decode_paged", "cg_stream_decode_paged", "cg_copy")
 
 
 def status_string(code: int) -> str:
@@ -250,6 +251,22 @@ def cg_decode_paged(shp, levels, tables, refs, n_refs, pool, num_blocks, block_t
                                _ptr(pool), int(num_blocks), _ptr(block_table), _ptr(status),
                                _prof(prof), _stream(stream))
     _check("cg_decode_paged", rc)
+
+
+def cg_stream_decode_paged(shp, levels, tables, records_host, offsets_host, table_of_record, n_records,
+                           staging, refs, pool, num_blocks, block_table, status, stream=None,
+                           copy_stream=None):
+    """records_host: pinned torch uint8 tensor; offsets_host: numpy uint64 [n+1];
+    table_of_record: numpy int32 [n] or None."""
+    arr, tp = _levels_and_tables(levels, tables)
+    offs = np.ascontiguousarray(offsets_host, dtype=np.uint64)
+    tor = None if table_of_record is None else np.ascontiguousarray(table_of_record, dtype=np.int32)
+    rc = lib().cg_stream_decode_paged(
+        ctypes.byref(shp), len(levels), arr, tp, _ptr(records_host), offs.ctypes.data,
+        None if tor is None else tor.ctypes.data, int(n_records), _ptr(staging),
+        staging.numel() * staging.element_size(), _ptr(refs), _ptr(pool), int(num_blocks),
+        _ptr(block_table), _ptr(status), _stream(stream), _stream(copy_stream))
+    _check("cg_stream_decode_paged", rc)
 
 
 def cg_copy(dst, src, nbytes, stream=None):

@@ -369,6 +369,74 @@ cg_status cg_decode_paged(const cg_shape* shape, int32_t n_levels, const cg_leve
   return hip_status(e);
 }
 
+cg_status cg_stream_decode_paged(const cg_shape* shape, int32_t n_levels, const cg_level* levels,
+                                 const void* const* tables_dev, const uint8_t* records_host,
+                                 const uint64_t* offsets_host, const int32_t* table_of_record_host,
+                                 int32_t n_records, uint8_t* staging_dev, uint64_t staging_bytes,
+                                 cg_chunk_ref* refs_dev, uint16_t* pool_dev, int64_t num_blocks,
+                                 const int32_t* block_table_dev, int32_t* status_dev,
+                                 hipStream_t stream, hipStream_t copy_stream) {
+  DecodeArgs a;
+  cg_status rc = decode_common(shape, n_levels, levels, tables_dev, refs_dev, 1, status_dev, &a);
+  if (rc != CG_OK) return rc;
+  if (!records_host || !offsets_host || n_records < 1 || !staging_dev || !aligned(staging_dev, 256) ||
+      !pool_dev || !aligned(pool_dev, 2) || num_blocks < 1 || num_blocks >= (1ll << 31) ||
+      !block_table_dev || !aligned(block_table_dev, 4))
+    return CG_ERR_INVALID_ARG;
+  if ((uint64_t)num_blocks * shape->kv_heads * 16 * shape->head_dim * 2 >= (1ull << 32))
+    return CG_ERR_UNSUPPORTED;
+  uint64_t max_rec = 0;
+  for (int32_t k = 0; k < n_records; ++k) {
+    if (offsets_host[k + 1] < offsets_host[k]) return CG_ERR_INVALID_ARG;
+    const uint64_t b = offsets_host[k + 1] - offsets_host[k];
+    if (b > max_rec) max_rec = b;
+    if (table_of_record_host && (table_of_record_host[k] < 0 || table_of_record_host[k] >= n_levels))
+      return CG_ERR_INVALID_ARG;
+  }
+  const uint64_t half = align_up(max_rec, 256);
+  if (2 * half > staging_bytes) return CG_ERR_INVALID_ARG;
+  a.pool = pool_dev;
+  a.num_blocks = num_blocks;
+  a.block_table = block_table_dev;
+
+  hipEvent_t copied[2] = {nullptr, nullptr}, consumed[2] = {nullptr, nullptr};
+  hipError_t e = hipSuccess;
+  for (int k = 0; k < 2 && e == hipSuccess; ++k) {
+    e = hipEventCreateWithFlags(&copied[k], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&consumed[k], hipEventDisableTiming);
+  }
+  if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(status_dev), 0, 1, stream);
+  // the first copy may only overwrite staging once earlier work on `stream` is done
+  if (e == hipSuccess) e = hipEventRecord(consumed[0], stream);
+  if (e == hipSuccess) e = hipEventRecord(consumed[1], stream);
+  for (int32_t k = 0; k < n_records && e == hipSuccess; ++k) {
+    const int slot = k & 1;
+    uint8_t* dst = staging_dev + slot * half;
+    const uint64_t bytes = offsets_host[k + 1] - offsets_host[k];
+    // receive: wait until the slot's previous record has been decoded
+    e = hipStreamWaitEvent(copy_stream, consumed[slot], 0);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(dst, records_host + offsets_host[k], bytes, hipMemcpyHostToDevice, copy_stream);
+    if (e == hipSuccess) e = hipEventRecord(copied[slot], copy_stream);
+    // decode + fill on `stream` once the record has landed
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, copied[slot], 0);
+    if (e == hipSuccess)
+      e = launch_set_ref(refs_dev + slot, dst, bytes, table_of_record_host ? table_of_record_host[k] : 0,
+                         stream);
+    if (e == hipSuccess) {
+      a.refs = refs_dev + slot;
+      a.n_refs = 1;
+      e = launch_decode(a, true, stream);
+    }
+    if (e == hipSuccess) e = hipEventRecord(consumed[slot], stream);
+  }
+  for (int k = 0; k < 2; ++k) {
+    if (copied[k]) hipEventDestroy(copied[k]);
+    if (consumed[k]) hipEventDestroy(consumed[k]);
+  }
+  return hip_status(e);
+}
+
 cg_status cg_copy(void* dst_dev, const void* src_dev, uint64_t bytes, hipStream_t stream) {
   if (!dst_dev || !src_dev || bytes % 16 != 0 || !aligned(dst_dev, 16) || !aligned(src_dev, 16))
     return CG_ERR_INVALID_ARG;

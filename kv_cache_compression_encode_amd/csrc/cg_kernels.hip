@@ -220,6 +220,17 @@ __global__ void k_make_refs(const uint8_t* base, const uint64_t* __restrict__ of
   }
 }
 
+__global__ void k_set_ref(cg_chunk_ref* ref, const uint8_t* record, uint64_t bytes, int32_t table) {
+  if (threadIdx.x == 0) {
+    cg_chunk_ref r;
+    r.record = record;
+    r.bytes = bytes;
+    r.table = table;
+    r.reserved = 0;
+    *ref = r;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // tables blob: header, steps, layer groups, quotient flags
 // ---------------------------------------------------------------------------
@@ -993,6 +1004,12 @@ hipError_t launch_make_refs(const uint8_t* base, const uint64_t* offs, int32_t n
                             cg_chunk_ref* refs, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_make_refs, dim3((n + 255) / 256), dim3(256), 0, st, base, offs, n, table, refs);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_ref(cg_chunk_ref* ref, const uint8_t* record, uint64_t bytes, int32_t table,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(k_set_ref, dim3(1), dim3(64), 0, st, ref, record, bytes, table);
   return hipGetLastError();
 }
 

@@ -204,5 +204,7 @@ hipError_t launch_decode(const DecodeArgs& a, bool paged, hipStream_t st);
 hipError_t launch_make_refs(const uint8_t* base, const uint64_t* offs, int32_t n, int32_t table,
                             cg_chunk_ref* refs, hipStream_t st);
 hipError_t launch_copy(void* dst, const void* src, uint64_t bytes, hipStream_t st);
+hipError_t launch_set_ref(cg_chunk_ref* ref, const uint8_t* record, uint64_t bytes, int32_t table,
+                          hipStream_t st);
 
 }  // namespace cg

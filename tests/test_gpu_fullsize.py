@@ -114,4 +114,24 @@ def test_stream_paged():
 
     F.check_slices(cfg, steps, X, y_slice, rng)
     blob = U.u8(tables[:cd.format_bytes(lv)])
-    F.check_groups(cfg, X, blob, lambda a, b: U.u8(out[a:b]), offs.cpu().numpy(), rng, n=3)
+    o = offs.cpu().numpy()
+    F.check_groups(cfg, X, blob, lambda a, b: U.u8(out[a:b]), o, rng, n=3)
+
+    # the same records streamed from pinned host memory into a second pool
+    host = torch.empty(int(o[-1]), dtype=torch.uint8).pin_memory()
+    host.copy_(out[:int(o[-1])].cpu())
+    staging = torch.empty(2 * int(np.diff(o).max()) + 512, dtype=torch.uint8, device="cuda")
+    refs2 = torch.empty(2 * C.REF_BYTES, dtype=torch.uint8, device="cuda")
+    pool2 = torch.empty_like(pool)
+    copy_stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    C.cg_stream_decode_paged(cd.shp, [lv], [tables], host, o.astype(np.uint64), None, n, staging, refs2,
+                             pool2, NB, torch.from_numpy(bt).cuda(), cd.status, copy_stream=copy_stream)
+    e1.record()
+    assert cd.read_status() == 0
+    ms = e0.elapsed_time(e1)
+    print("streamed %d records, %.1f MB in %.2f ms (%.1f GB/s host-to-device incl. decode)" % (
+        n, o[-1] / 1e6, ms, o[-1] / ms / 1e6), flush=True)
+    assert torch.equal(pool2.view(torch.int16), pool.view(torch.int16))

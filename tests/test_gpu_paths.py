@@ -172,3 +172,37 @@ def test_repeat_is_deterministic(multi):
         out, offs = cd.encode(x, gl[2], t)
         o = offs.cpu().numpy()
         assert np.array_equal(U.u8(out)[:int(o[-1])], U.u8(outs[2][0])[:int(o[-1])])
+
+
+def test_stream_decode_paged_pipeline(multi):
+    """Records copied from pinned host memory on a second stream while the
+    previous record decodes ("CacheGen实战" 2.3 pipeline); same pool as the
+    oracle's paged decode."""
+    cfg, X, cd, gl, tabs, outs, oshp, oracle = multi
+    NB = cfg.tokens // 16 + 3
+    bt = np.random.default_rng(9).permutation(NB)[:cfg.tokens // 16].astype(np.int32)
+    mix = np.array([1, 2, 0, 1], dtype=np.int32)
+    # host-side stream of records, each from its chunk's level
+    recs = []
+    for c, m in enumerate(mix):
+        out, offs = outs[int(m)]
+        o = offs.cpu().numpy()
+        recs.append(U.u8(out[int(o[c]):int(o[c + 1])]))
+    host_offs = np.zeros(len(recs) + 1, dtype=np.uint64)
+    for k, r in enumerate(recs):
+        host_offs[k + 1] = host_offs[k] + len(r)
+    host = torch.empty(int(host_offs[-1]), dtype=torch.uint8).pin_memory()
+    host.copy_(torch.from_numpy(np.concatenate(recs)))
+    staging = torch.empty(2 * int(max(len(r) for r in recs)) + 512, dtype=torch.uint8, device="cuda")
+    refs = torch.empty(2 * C.REF_BYTES, dtype=torch.uint8, device="cuda")
+    pool = torch.full((cfg.layers, 2, NB, cfg.kv_heads, 16, cfg.head_dim), 0x7BFF, dtype=torch.int16,
+                      device="cuda")
+    copy_stream = torch.cuda.Stream()
+    C.cg_stream_decode_paged(cd.shp, gl, tabs, host, host_offs, mix, len(recs), staging, refs, pool, NB,
+                             torch.from_numpy(bt).cuda(), cd.status, copy_stream=copy_stream)
+    assert cd.read_status() == 0
+    opool = np.full(pool.shape, 0x7BFF, dtype=np.uint16)
+    for c, m in enumerate(mix):
+        blob, data, ooffs = oracle[int(m)]
+        assert O.decode_chunk_paged(oshp, blob, data[int(ooffs[c]):int(ooffs[c + 1])], opool, bt) == O.OK
+    assert np.array_equal(pool.cpu().numpy().view(np.uint16), opool)
