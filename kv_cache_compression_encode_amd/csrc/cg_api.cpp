@@ -297,6 +297,46 @@ cg_status cg_make_refs(const uint8_t* base_dev, const uint64_t* offsets_dev, int
   return hip_status(launch_make_refs(base_dev, offsets_dev, n, table, refs_dev, stream));
 }
 
+static int compute_units() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return 256;
+  return cus;
+}
+
+// Records per decode workgroup when every record uses one table set. A
+// workgroup holds R records x (layers of its group) groups, dealt to its 16
+// wavefronts, so a wavefront runs c = ceil(items / 16) <= 3 interleaved
+// chains. One workgroup fits a compute unit (its tables fill the LDS), so
+// the decode takes about ceil(workgroups / CUs) rounds, each as long as a
+// wavefront's c-chain step. Relative step times (1 chain = 100) are measured
+// on gfx950; the R with the least rounds x step time wins.
+static int refs_per_block(const Shape& s, const cg_level& lv, int32_t n_refs) {
+  static const int kStepCost[kChains + 1] = {0, 100, 168, 215};
+  int lg_max = 0;
+  for (int g = 0; g < lv.n_groups; ++g) {
+    int n = 0;
+    for (int l = 0; l < s.L; ++l) n += lv.layer_group[l] == g;
+    if (n > lg_max) lg_max = n;
+  }
+  const uint64_t sets = (uint64_t)lv.n_groups * 2 * s.H * s.S;
+  const uint64_t cus = (uint64_t)compute_units();
+  int best = 1;
+  uint64_t best_cost = ~0ull;
+  for (int r = 1; r <= kMaxRefsPerBlock && r <= n_refs; ++r) {
+    const int chains = (r * lg_max + kWaves - 1) / kWaves;
+    if (chains > kChains) break;
+    const uint64_t wgs = (uint64_t)((n_refs + r - 1) / r) * sets;
+    const uint64_t cost = (wgs + cus - 1) / cus * (uint64_t)kStepCost[chains < 1 ? 1 : chains];
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = r;
+    }
+  }
+  return best;
+}
+
 static cg_status decode_common(const cg_shape* shape, int32_t n_levels, const cg_level* levels,
                                const void* const* tables_dev, const cg_chunk_ref* refs_dev,
                                int32_t n_refs, int32_t* status_dev, DecodeArgs* a) {
@@ -323,6 +363,7 @@ static cg_status decode_common(const cg_shape* shape, int32_t n_levels, const cg
   a->s = s;
   a->refs = refs_dev;
   a->n_refs = n_refs;
+  a->refs_per_block = n_levels == 1 ? refs_per_block(s, levels[0], n_refs) : 1;
   a->n_tables = n_levels;
   a->g_max = g_max;
   a->status = status_dev;
@@ -431,8 +472,8 @@ cg_status cg_stream_decode_paged(const cg_shape* shape, int32_t n_levels, const 
     if (e == hipSuccess) e = hipEventRecord(consumed[slot], stream);
   }
   for (int k = 0; k < 2; ++k) {
-    if (copied[k]) hipEventDestroy(copied[k]);
-    if (consumed[k]) hipEventDestroy(consumed[k]);
+    if (copied[k]) (void)hipEventDestroy(copied[k]);
+    if (consumed[k]) (void)hipEventDestroy(consumed[k]);
   }
   return hip_status(e);
 }

@@ -761,22 +761,25 @@ __global__ void __launch_bounds__(kWriteThreads) k_write(WriteArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// decode: one workgroup per (record, layer group, K|V, head, slice); the
-// set's decoder tables (lane-minor, 128 KB) sit in LDS and each wavefront
-// decodes the group of one layer at a time. Per wavefront a 512-word LDS ring
-// (+ 64-word mirror) holds the stream, refilled 256 words ahead with
-// coalesced 8-byte loads.
+// decode: one workgroup per (block of records, layer group, K|V, head, slice).
+// The set's decoder tables (lane-minor, 128 KB) sit in LDS. The workgroup's
+// groups (records x layers of the layer group) are dealt to the wavefronts
+// round-robin, so a wavefront holds up to three; it decodes them as
+// independent chains interleaved in one instruction stream, so the dependent
+// LDS reads of one chain overlap the others'. Per chain a 256-word LDS ring
+// (+ 64-word mirror) holds the stream, refilled 128 words ahead with one
+// coalesced dword per lane.
 //
-// Per token and lane (x = rANS state, slot = x & 4095):
-//   w = slot >> 5; rank = rankbase[w] + popcount(bitmap[w] << (31 - (slot & 31)))
-//   info = sym | (4096 - f) << 8 | b << 20
+// Per token and lane (x = rANS state, slot = x & 4095, w = slot >> 5):
+//   info = LDS[rankx[w] - 256 * popcount(above[w] << (slot & 31))]
+//        = d | (4096 - f) << 8 | b << 20
 //   x = x - ((4096 - f) * (x >> 12) + b)      (= f * (x >> 12) + slot - b)
 //   x < 2^16: x = x << 16 | next renorm word (ballot + mbcnt)
-//   sym 255: d = next escape payload, else d = sym - 127
-//   q = q + d (mod 2^16); y = fp16(fl32(q * step))
+//   q += d (signed byte); byte 0x80: q += 128 + escape payload
+//   y = fp16(fl32(q * step))
 // ---------------------------------------------------------------------------
 constexpr int kDecThreads = kWaves * 64;
-constexpr int kRingStride = kRingWords + kRingMirror;  // 16-bit words per wavefront
+constexpr int kRingStride = kRingWords + kRingMirror;  // 16-bit words per chain
 
 // a * b + c on 24-bit signed operands in one instruction (the compiler would
 // split a multiply by -256 into a shift and a subtraction)
@@ -790,113 +793,404 @@ __device__ __forceinline__ uint32_t lds_u32(const uint32_t* base, uint32_t byte_
   return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(base) + byte_off);
 }
 
+// x = x << 16 | w on the lanes of m only, the other lanes unchanged: one VALU
+// instruction under a narrowed execution mask instead of a shift and a select.
+__device__ __forceinline__ void renorm_lanes(uint32_t& x, uint32_t w, uint64_t m) {
+  uint64_t saved;
+  asm volatile(
+      "s_and_saveexec_b64 %1, %2\n\t"
+      "v_lshl_or_b32 %0, %0, 16, %3\n\t"
+      "s_mov_b64 exec, %1"
+      : "+v"(x), "=&s"(saved)
+      : "s"(m), "v"(w)
+      : "scc");
+}
+
+struct Chain {
+  __amdgpu_buffer_rsrc_t src;  // the group's padded stream (reads past it give 0)
+  __amdgpu_buffer_rsrc_t dst;  // output rows
+  uint16_t* ring;
+  uint32_t p, loaded, nw;      // words consumed / staged / in the stream
+  uint32_t doff;               // byte offset of the current output row in dst
+  uint32_t pref;               // per lane: the next 128-word block, one dword each
+  uint32_t x, q;               // per lane: rANS state, token value mod 2^16
+  int64_t t0;
+  int n;
+  uint32_t bt0, bt1;           // paged: block-table entries of blocks bt_base + lane, + 64
+  int64_t bt_base;
+  bool ok;
+  // values carried between the phases of one token (pipelined loop)
+  uint32_t above, rankx, info, w;
+  uint64_t mr;
+};
+
+struct GroupRef {
+  const uint8_t* rec;
+  uint64_t ds, dbytes;
+  int64_t t0;
+  int n;
+  int l;
+};
+
 template <bool PAGED>
-__device__ __forceinline__ void decode_group(const DecodeArgs& a, const uint32_t* tabs,
-                                             uint16_t* ring, const uint8_t* __restrict__ rec,
-                                             uint64_t ds, uint64_t data_bytes, int64_t gpc, int l,
-                                             int kv, int h, int j, int64_t t0, int64_t n,
-                                             float step, int lane) {
+__device__ __forceinline__ uint32_t row_offset(const DecodeArgs& a, Chain& c, int64_t t, int h,
+                                               uint32_t row_bytes, int lane) {
+  if (!PAGED) return (uint32_t)(t - c.t0) * row_bytes;
+  const int64_t b = (t >> 4) - c.bt_base;
+  if (b >= 128) {  // next window of 128 block-table entries
+    c.bt_base += 128;
+    const int64_t i0 = c.bt_base + lane, i1 = c.bt_base + 64 + lane;
+    const int64_t last = (c.t0 + c.n - 1) >> 4;
+    c.bt0 = i0 <= last ? (uint32_t)a.block_table[i0] : 0u;
+    c.bt1 = i1 <= last ? (uint32_t)a.block_table[i1] : 0u;
+    // wait here, once per 2048 tokens, so the compiler does not have to
+    // assume these loads pending (and wait for every store) on each step
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  }
+  const uint32_t bi = (uint32_t)((t >> 4) - c.bt_base);
+  const uint32_t blk = bi < 64 ? (uint32_t)__builtin_amdgcn_readlane(c.bt0, bi)
+                               : (uint32_t)__builtin_amdgcn_readlane(c.bt1, bi - 64);
+  return ((blk * (uint32_t)a.s.H + (uint32_t)h) * 16u + (uint32_t)(t & 15)) * row_bytes;
+}
+
+__device__ __forceinline__ void ring_put(Chain& c, uint32_t wbase, uint32_t v, int lane) {
+  const uint32_t r = (wbase + 2u * lane) & (kRingWords - 1);
+  *reinterpret_cast<uint32_t*>(c.ring + r) = v;
+  if (r < (uint32_t)kRingMirror) *reinterpret_cast<uint32_t*>(c.ring + kRingWords + r) = v;
+}
+
+__device__ __forceinline__ uint32_t stream_load(const Chain& c, uint32_t wbase, int lane) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(c.src, 4u * lane, 2u * wbase, 0);
+}
+
+// Sets up one group: checks its directory entry, stages its first 256 words,
+// reads the head and writes token 0. c.ok = false for a damaged entry.
+template <bool PAGED>
+__device__ __forceinline__ void chain_open(const DecodeArgs& a, Chain& c, const GroupRef& gr,
+                                           int64_t gpc, int kv, int h, int j, float step,
+                                           uint16_t* ring, int lane) {
   const Shape s = a.s;
-  const int64_t gi = (((int64_t)l * 2 + kv) * s.H + h) * s.S + j;
-  const uint64_t* goffs = reinterpret_cast<const uint64_t*>(rec + 64);
-  const uint32_t* gwords = reinterpret_cast<const uint32_t*>(rec + 64 + 8 * (gpc + 1));
+  c.ok = false;
+  const int64_t gi = (((int64_t)gr.l * 2 + kv) * s.H + h) * s.S + j;
+  const uint64_t* goffs = reinterpret_cast<const uint64_t*>(gr.rec + 64);
+  const uint32_t* gwords = reinterpret_cast<const uint32_t*>(gr.rec + 64 + 8 * (gpc + 1));
   const uint64_t o0 = uni(goffs[gi]), o1 = uni(goffs[gi + 1]);
   const uint32_t nw = uni(gwords[gi]);
-  if ((o0 & 15) || (o1 & 15) || o0 > o1 || o1 > data_bytes || 2ull * nw > o1 - o0 ||
+  if ((o0 & 15) || (o1 & 15) || o0 > o1 || o1 > gr.dbytes || 2ull * nw > o1 - o0 ||
       nw < (uint32_t)kHdrWords || (o1 - o0) >= (1ull << 32) || (gi == 0 && o0 != 0) ||
-      (gi == gpc - 1 && o1 != data_bytes)) {
+      (gi == gpc - 1 && o1 != gr.dbytes)) {
     if (lane == 0) set_status(a.status, CG_ERR_CORRUPT);
     return;
   }
-  // the group's stream: words past its padded end read as 0
-  const __amdgpu_buffer_rsrc_t src = make_rsrc(rec + ds + o0, (uint32_t)(o1 - o0));
-  const uint32_t lane8 = 8u * lane;
-  auto load4 = [&](uint32_t wbase) -> uint2 {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(src, lane8, 2 * wbase, 0);
-    return make_uint2(v[0], v[1]);
-  };
-  // words [wbase, wbase+256) -> ring; block 0 also refreshes the mirror of words 0..63
-  auto put4 = [&](uint32_t wbase, uint2 v) {
-    const uint32_t r = (wbase + 4u * lane) & (kRingWords - 1);
-    *reinterpret_cast<uint2*>(ring + r) = v;
-    if (r < (uint32_t)kRingMirror) *reinterpret_cast<uint2*>(ring + kRingWords + r) = v;
-  };
+  c.ok = true;
+  c.src = make_rsrc(gr.rec + gr.ds + o0, (uint32_t)(o1 - o0));
+  c.ring = ring;
+  c.nw = nw;
+  c.t0 = gr.t0;
+  c.n = gr.n;
   {
-    const uint2 v0 = load4(0), v1 = load4(256);
-    put4(0, v0);
-    put4(256, v1);
+    const uint32_t v0 = stream_load(c, 0, lane), v1 = stream_load(c, kRingBlock, lane);
+    ring_put(c, 0, v0, lane);
+    ring_put(c, kRingBlock, v1, lane);
   }
-  uint32_t loaded = 512;
-  uint2 pref = load4(512);
+  c.loaded = 2 * kRingBlock;
+  c.pref = stream_load(c, c.loaded, lane);
   __builtin_amdgcn_wave_barrier();
-
-  uint32_t x = ((uint32_t)ring[lane] << 16) | ring[64 + lane];
-  uint32_t q = ring[128 + lane];  // q modulo 2^16 lives in the low half
-  uint32_t p = kHdrWords;
-  const uint32_t lane4 = 4u * lane;
-  constexpr uint32_t kRbOff = 4u * (kDecRb - kDecBm);
-
-  // destination rows: contiguous y[l][kv][h][t][64j ..] or pool[l][kv][blk][h][t%16][64j ..]
-  const uint32_t lane2 = 2u * lane;
+  c.x = ((uint32_t)ring[lane] << 16) | ring[64 + lane];
+  c.q = ring[128 + lane];
+  c.p = kHdrWords;
   const uint32_t row_bytes = 2u * (uint32_t)s.D;
-  __amdgpu_buffer_rsrc_t dst;
-  uint32_t doff = 0;
   const size_t col = (size_t)64 * j;
   if (!PAGED) {
-    const uint16_t* y0 = a.y + ((((size_t)l * 2 + kv) * s.H + h) * (size_t)s.T + t0) * s.D + col;
-    dst = make_rsrc(y0, (uint32_t)(n * row_bytes));
+    const uint16_t* y0 = a.y + ((((size_t)gr.l * 2 + kv) * s.H + h) * (size_t)s.T + gr.t0) * s.D + col;
+    c.dst = make_rsrc(y0, (uint32_t)(gr.n * row_bytes));
   } else {
-    const uint16_t* p0 = a.pool + ((size_t)l * 2 + kv) * (size_t)a.num_blocks * s.H * 16 * s.D + col;
-    dst = make_rsrc(p0, (uint32_t)((uint64_t)a.num_blocks * s.H * 16 * row_bytes));
+    const uint16_t* p0 = a.pool + ((size_t)gr.l * 2 + kv) * (size_t)a.num_blocks * s.H * 16 * s.D + col;
+    c.dst = make_rsrc(p0, (uint32_t)((uint64_t)a.num_blocks * s.H * 16 * row_bytes));
+    c.bt_base = gr.t0 >> 4;
+    const int64_t last = (gr.t0 + gr.n - 1) >> 4;
+    const int64_t i0 = c.bt_base + lane, i1 = c.bt_base + 64 + lane;
+    c.bt0 = i0 <= last ? (uint32_t)a.block_table[i0] : 0u;
+    c.bt1 = i1 <= last ? (uint32_t)a.block_table[i1] : 0u;
   }
-  auto pool_off = [&](int64_t t) -> uint32_t {
-    const uint32_t blk = (uint32_t)__builtin_amdgcn_readfirstlane(a.block_table[t >> 4]);
-    return ((blk * (uint32_t)s.H + (uint32_t)h) * 16u + (uint32_t)(t & 15)) * row_bytes;
-  };
-  if (PAGED) doff = pool_off(t0);
-  __builtin_amdgcn_raw_buffer_store_b16(dequantize_low16(q, step), dst, lane2, doff, 0);
+  c.doff = row_offset<PAGED>(a, c, gr.t0, h, row_bytes, lane);
+  __builtin_amdgcn_raw_buffer_store_b16(dequantize_low16(c.q, step), c.dst, 2u * lane, c.doff, 0);
+}
 
-  for (int i = 1; i < (int)n; ++i) {
-    if (loaded - p < 256u) {
-      put4(loaded, pref);
-      loaded += 256;
-      pref = load4(loaded);
+__device__ __forceinline__ void chain_close(const DecodeArgs& a, const Chain& c, int lane) {
+  const bool bad = (__ballot(c.x != kL) != 0) || (c.p != c.nw);
+  if (bad && lane == 0) set_status(a.status, CG_ERR_CORRUPT);
+}
+
+// Tokens [i_begin, i_end) of NC chains in lockstep.
+template <bool PAGED, int NC>
+__device__ __forceinline__ void chain_steps(const DecodeArgs& a, Chain* c, int i_begin, int i_end,
+                                            const uint32_t* tabs, int h, float step, int lane) {
+  const uint32_t lane4 = 4u * lane, lane2 = 2u * lane;
+  constexpr uint32_t kRbOff = 4u * (kDecRb - kDecBm);
+  const uint32_t row_bytes = 2u * (uint32_t)a.s.D;
+  // Retire every outstanding vector-memory load before the loop, so no load
+  // issued by an earlier loop is still pending on a register this loop reuses
+  // (that would put a vmcnt wait on every step). vmcnt(0), expcnt/lgkmcnt
+  // unrestricted.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  for (int i = i_begin; i < i_end; ++i) {
+    bool refill = false;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) refill |= c[k].loaded - c[k].p < (uint32_t)kRingBlock;
+    if (refill) {
+#pragma unroll
+      for (int k = 0; k < NC; ++k) {
+        if (c[k].loaded - c[k].p < (uint32_t)kRingBlock) {
+          ring_put(c[k], c[k].loaded, c[k].pref, lane);
+          c[k].loaded += kRingBlock;
+          c[k].pref = stream_load(c[k], c[k].loaded, lane);
+        }
+      }
       __builtin_amdgcn_wave_barrier();
     }
-    // slot -> (d, 4096 - f, b)
-    const uint32_t ob = ((x << 3) & 0x7F00u) | lane4;  // word (slot >> 5) of this lane
-    const uint32_t above = lds_u32(tabs, ob), rankx = lds_u32(tabs, ob + kRbOff);
-    const uint32_t after = (uint32_t)__popc(above << (x & 31u));  // starts after the slot
-    const uint32_t info = lds_u32(tabs, mad_i24(after, -256, rankx));
-    const uint32_t fp = (info >> 8) & 0xFFFu, bs = info >> 20;
-    x = x - (fp * (x >> 12) + bs);
-    // renormalise
-    const bool need = x < kL;
-    const uint64_t mr = __ballot(need);
-    const uint16_t* rp = ring + (p & (kRingWords - 1));
-    if (need) x = (x << 16) | rp[mbcnt_base(mr, 0)];
-    p += (uint32_t)__popcll(mr);
-    // token prefix: q += d, or the escape payload (the byte 0x80 added -128)
-    q += (uint32_t)(int32_t)(int8_t)(info & 0xFFu);
-    const bool is_esc = (info & 0xFFu) == 0x80u;
-    const uint64_t me = __ballot(is_esc);
-    if (me) {
-      const uint16_t* ep = ring + (p & (kRingWords - 1));
-      if (is_esc) q += 128u + ep[mbcnt_base(me, 0)];  // payload = difference mod 2^16
-      p += (uint32_t)__popcll(me);
+    // The three dependent LDS reads of a token are issued chain by chain in
+    // phases; a scheduling fence after each phase keeps the compiler from
+    // serialising the chains (it would otherwise finish one chain's read
+    // chain before starting the next one's).
+    uint32_t above[NC], rankx[NC], info[NC], w[NC];
+    uint64_t mr[NC];
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      const uint32_t ob = ((c[k].x << 3) & 0x7F00u) | lane4;  // word (slot >> 5) of this lane
+      above[k] = lds_u32(tabs, ob);
+      rankx[k] = lds_u32(tabs, ob + kRbOff);
     }
-    const uint16_t y = dequantize_low16(q, step);
-    doff = PAGED ? pool_off(t0 + i) : doff + row_bytes;
-    __builtin_amdgcn_raw_buffer_store_b16(y, dst, lane2, doff, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      const uint32_t after = (uint32_t)__popc(above[k] << (c[k].x & 31u));  // starts after the slot
+      info[k] = lds_u32(tabs, mad_i24(after, -256, rankx[k]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      const uint32_t x = c[k].x;
+      const uint32_t fp = (info[k] >> 8) & 0xFFFu, bs = info[k] >> 20;
+      c[k].x = x - (fp * (x >> 12) + bs);
+      mr[k] = __ballot(c[k].x < kL);
+      const uint16_t* rp = c[k].ring + (c[k].p & (kRingWords - 1));
+      w[k] = rp[mbcnt_base(mr[k], 0)];  // every lane reads; only renormalising lanes use it
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      renorm_lanes(c[k].x, w[k], mr[k]);
+      c[k].p += (uint32_t)__popcll(mr[k]);
+      c[k].q += (uint32_t)(int32_t)(int8_t)(info[k] & 0xFFu);
+    }
+    uint64_t me[NC];
+    bool any_esc = false;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      me[k] = __ballot((info[k] & 0xFFu) == 0x80u);
+      any_esc |= me[k] != 0;
+    }
+    if (any_esc) {
+#pragma unroll
+      for (int k = 0; k < NC; ++k) {
+        if (me[k]) {
+          const uint16_t* ep = c[k].ring + (c[k].p & (kRingWords - 1));
+          if ((info[k] & 0xFFu) == 0x80u) c[k].q += 128u + ep[mbcnt_base(me[k], 0)];
+          c[k].p += (uint32_t)__popcll(me[k]);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      const uint16_t y = dequantize_low16(c[k].q, step);
+      if (PAGED)
+        c[k].doff = row_offset<PAGED>(a, c[k], c[k].t0 + i, h, row_bytes, lane);
+      else
+        c[k].doff += row_bytes;
+      __builtin_amdgcn_raw_buffer_store_b16(y, c[k].dst, lane2, c[k].doff, 0);
+    }
   }
-  const bool bad = (__ballot(x != kL) != 0) || (p != nw);
-  if (bad && lane == 0) set_status(a.status, CG_ERR_CORRUPT);
+}
+
+// ---- software-pipelined chains ---------------------------------------------
+// A token of one chain is three phases, each ending in one LDS read that the
+// next phase consumes:
+//   A: (refill the ring) and read above/rankx of the state's slot word
+//   B: read the info entry
+//   C: update the state, ballot the lanes that renormalise, read their words
+//   D: (consumes C's read) renormalise, advance q, escapes, store the row
+// D of a token and A of the next need no LDS round trip between them, so a
+// token is three slots. Chain k runs k slots behind chain 0; every slot holds
+// one phase of every chain, so each LDS read is covered by a full slot of the
+// other chains' work instead of being waited for at once.
+
+__device__ __forceinline__ void ph_a(Chain& c, const uint32_t* tabs, int lane) {
+  if (c.loaded - c.p < (uint32_t)kRingBlock) {
+    ring_put(c, c.loaded, c.pref, lane);
+    c.loaded += kRingBlock;
+    c.pref = stream_load(c, c.loaded, lane);
+    __builtin_amdgcn_wave_barrier();
+  }
+  const uint32_t ob = ((c.x << 3) & 0x7F00u) | (4u * lane);  // word (slot >> 5) of this lane
+  c.above = lds_u32(tabs, ob);
+  c.rankx = lds_u32(tabs, ob + 4u * (kDecRb - kDecBm));
+}
+
+__device__ __forceinline__ void ph_b(Chain& c, const uint32_t* tabs) {
+  const uint32_t after = (uint32_t)__popc(c.above << (c.x & 31u));  // starts after the slot
+  c.info = lds_u32(tabs, mad_i24(after, -256, c.rankx));
+}
+
+__device__ __forceinline__ void ph_c(Chain& c) {
+  const uint32_t x = c.x;
+  const uint32_t fp = (c.info >> 8) & 0xFFFu, bs = c.info >> 20;
+  c.x = x - (fp * (x >> 12) + bs);
+  c.mr = __ballot(c.x < kL);
+  const uint16_t* rp = c.ring + (c.p & (kRingWords - 1));
+  c.w = rp[mbcnt_base(c.mr, 0)];  // every lane reads; only renormalising lanes use it
+}
+
+template <bool PAGED>
+__device__ __forceinline__ void ph_d(const DecodeArgs& a, Chain& c, int i, int h, float step,
+                                     uint32_t row_bytes, int lane) {
+  renorm_lanes(c.x, c.w, c.mr);
+  c.p += (uint32_t)__popcll(c.mr);
+  c.q += (uint32_t)(int32_t)(int8_t)(c.info & 0xFFu);
+  const uint64_t me = __ballot((c.info & 0xFFu) == 0x80u);
+  if (me) {
+    const uint16_t* ep = c.ring + (c.p & (kRingWords - 1));
+    if ((c.info & 0xFFu) == 0x80u) c.q += 128u + ep[mbcnt_base(me, 0)];
+    c.p += (uint32_t)__popcll(me);
+  }
+  const uint16_t y = dequantize_low16(c.q, step);
+  if (PAGED)
+    c.doff = row_offset<PAGED>(a, c, c.t0 + i, h, row_bytes, lane);
+  else
+    c.doff += row_bytes;
+  __builtin_amdgcn_raw_buffer_store_b16(y, c.dst, 2u * lane, c.doff, 0);
+}
+
+#define CG_SLOT __builtin_amdgcn_sched_barrier(0)
+
+// Tokens [i0, i1) of NC = 2 or 3 chains, i1 > i0, software-pipelined. A
+// scheduling fence after every phase keeps each phase's LDS read where it is
+// issued (the compiler would sink the reads to the end of a slot).
+template <bool PAGED, int NC>
+__device__ __forceinline__ void chain_pipe(const DecodeArgs& a, Chain* c, int i0, int i1,
+                                           const uint32_t* tabs, int h, float step, int lane) {
+  static_assert(NC == 2 || NC == 3, "two or three chains");
+  const uint32_t row_bytes = 2u * (uint32_t)a.s.D;
+  // see chain_steps: no load of an earlier loop may stay pending
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  // prologue: chain 0 runs A, B, C of token i0; chain 1 A, B; chain 2 A
+  ph_a(c[0], tabs, lane);
+  CG_SLOT;
+  ph_b(c[0], tabs);
+  CG_SLOT;
+  ph_a(c[1], tabs, lane);
+  CG_SLOT;
+  ph_c(c[0]);
+  CG_SLOT;
+  ph_b(c[1], tabs);
+  CG_SLOT;
+  if (NC == 3) {
+    ph_a(c[2], tabs, lane);
+    CG_SLOT;
+  }
+  for (int i = i0; i < i1 - 1; ++i) {
+    ph_d<PAGED>(a, c[0], i, h, step, row_bytes, lane);
+    ph_a(c[0], tabs, lane);
+    CG_SLOT;
+    ph_c(c[1]);
+    CG_SLOT;
+    if (NC == 3) {
+      ph_b(c[2], tabs);
+      CG_SLOT;
+    }
+    ph_b(c[0], tabs);
+    CG_SLOT;
+    ph_d<PAGED>(a, c[1], i, h, step, row_bytes, lane);
+    ph_a(c[1], tabs, lane);
+    CG_SLOT;
+    if (NC == 3) {
+      ph_c(c[2]);
+      CG_SLOT;
+    }
+    ph_c(c[0]);
+    CG_SLOT;
+    ph_b(c[1], tabs);
+    CG_SLOT;
+    if (NC == 3) {
+      ph_d<PAGED>(a, c[2], i, h, step, row_bytes, lane);
+      ph_a(c[2], tabs, lane);
+      CG_SLOT;
+    }
+  }
+  // epilogue: finish token i1 - 1
+  ph_d<PAGED>(a, c[0], i1 - 1, h, step, row_bytes, lane);
+  ph_c(c[1]);
+  if (NC == 3) ph_b(c[2], tabs);
+  ph_d<PAGED>(a, c[1], i1 - 1, h, step, row_bytes, lane);
+  if (NC == 3) {
+    ph_c(c[2]);
+    ph_d<PAGED>(a, c[2], i1 - 1, h, step, row_bytes, lane);
+  }
+}
+
+// The k-th layer (0-based, ascending) of layer group g, or -1; computed by
+// one wavefront with ballots over the blob's layer -> group map.
+__device__ __forceinline__ int layer_of_group(const uint8_t* blob, int G, int L, int g, int k, int lane) {
+  int base = 0;
+  for (int l0 = 0; l0 < L; l0 += 64) {
+    const int l = l0 + lane;
+    const bool in = l < L && blob_lg(blob, G)[l < L ? l : 0] == g;
+    const uint64_t m = __ballot(in);
+    const int cnt = __popcll(m);
+    if (k < base + cnt) {
+      const uint64_t hit = __ballot(in && (int)mbcnt_base(m, 0) == k - base);
+      return l0 + __builtin_ctzll(hit);
+    }
+    base += cnt;
+  }
+  return -1;
+}
+
+__device__ __forceinline__ int layers_in_group(const uint8_t* blob, int G, int L, int g, int lane) {
+  int n = 0;
+  for (int l0 = 0; l0 < L; l0 += 64) {
+    const int l = l0 + lane;
+    n += __popcll(__ballot(l < L && blob_lg(blob, G)[l < L ? l : 0] == g));
+  }
+  return n;
+}
+
+// NC chains decoded together for their common length, then the longer ones
+// finish one at a time.
+template <bool PAGED, int NC>
+__device__ __forceinline__ void run_chains(const DecodeArgs& a, Chain* c, const uint32_t* tabs,
+                                           int h, float step, int lane) {
+  int nmin = c[0].n;
+#pragma unroll
+  for (int k = 1; k < NC; ++k) nmin = c[k].n < nmin ? c[k].n : nmin;
+  if constexpr (NC == 1) {
+    chain_steps<PAGED, 1>(a, c, 1, nmin, tabs, h, step, lane);
+  } else {
+    if (nmin > 1) chain_pipe<PAGED, NC>(a, c, 1, nmin, tabs, h, step, lane);
+  }
+  if constexpr (NC > 1) {
+#pragma unroll
+    for (int k = 0; k < NC; ++k)
+      if (c[k].n > nmin) chain_steps<PAGED, 1>(a, &c[k], nmin > 1 ? nmin : 1, c[k].n, tabs, h, step, lane);
+  }
+#pragma unroll
+  for (int k = 0; k < NC; ++k) chain_close(a, c[k], lane);
 }
 
 template <bool PAGED>
 __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
   __shared__ uint32_t tabs[kDecDwords * 64];
-  __shared__ uint16_t rings[kWaves * kRingStride];
+  __shared__ uint16_t rings[kWaves * kChains * kRingStride];
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const Shape s = a.s;
   int64_t bid = blockIdx.x;
@@ -907,12 +1201,13 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
   const int kv = (int)(bid % 2);
   bid /= 2;
   const int g = (int)(bid % a.g_max);
-  const int64_t r = bid / a.g_max;
+  const int64_t rb = bid / a.g_max;
+  const int64_t r_begin = rb * a.refs_per_block;
+  const int64_t r_end = r_begin + a.refs_per_block < a.n_refs ? r_begin + a.refs_per_block : a.n_refs;
   const bool first_block = (g == 0 && kv == 0 && h == 0 && j == 0);
 
-  const uint8_t* rec = uni(a.refs[r].record);
-  const uint64_t ref_bytes = uni(a.refs[r].bytes);
-  const int ti = uni(a.refs[r].table);
+  // all records of a workgroup use the first one's table set
+  const int ti = uni(a.refs[r_begin].table);
   if (ti < 0 || ti >= a.n_tables) {
     if (tid == 0 && first_block) set_status(a.status, CG_ERR_INVALID_ARG);
     return;
@@ -925,55 +1220,102 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
     if (tid == 0) set_status(a.status, CG_ERR_INVALID_ARG);
     return;
   }
-  // record header
   const int64_t gpc = groups_per_chunk(s.L, s.H, s.D);
   const uint64_t ds_expect = rec_data_start(gpc);
-  if (ref_bytes < ds_expect || (reinterpret_cast<uintptr_t>(rec) & 15)) {
-    if (tid == 0) set_status(a.status, CG_ERR_CORRUPT);
-    return;
-  }
-  const uint32_t* rh = reinterpret_cast<const uint32_t*>(rec);
-  const int64_t c = uni(rh[2]);
   const int64_t nch = n_chunks(s.T, s.C);
-  const uint64_t rbytes = uni(*reinterpret_cast<const uint64_t*>(rec + 48));
-  const uint64_t dbytes = uni(*reinterpret_cast<const uint64_t*>(rec + 56));
-  bool bad = uni(rh[0]) != kRecordMagic || uni(rh[1]) != kVersion || c >= nch ||
-             (int32_t)uni(rh[3]) != a.level_id[ti];
-  if (!bad) {
-    bad = uni(*reinterpret_cast<const uint64_t*>(rec + 16)) != (uint64_t)(c * s.C) ||
-          uni(rh[6]) != (uint32_t)chunk_len(s.T, s.C, c) || uni(rh[7]) != (uint32_t)gpc ||
-          (int)uni(rh[8]) != s.L || (int)uni(rh[9]) != s.H || (int)uni(rh[10]) != s.D ||
-          uni(rh[11]) != ds_expect || rbytes > ref_bytes || ds_expect + dbytes > rbytes;
-  }
-  if (bad) {
-    if (tid == 0) set_status(a.status, CG_ERR_CORRUPT);
-    return;
-  }
-  const int64_t n = chunk_len(s.T, s.C, c), t0 = c * s.C;
-  if (PAGED) {
-    bool bt_bad = false;
-    for (int64_t b = (t0 >> 4) + tid; b <= ((t0 + n - 1) >> 4); b += kDecThreads) {
-      const int32_t v = a.block_table[b];
-      bt_bad |= (v < 0 || (int64_t)v >= a.num_blocks);
+
+  // record headers of this workgroup (at most kMaxRefsPerBlock = 3)
+  GroupRef rr0, rr1, rr2;
+  rr0.l = rr1.l = rr2.l = 0;
+  int nrec = 0;
+  for (int64_t r = r_begin; r < r_end && nrec < kMaxRefsPerBlock; ++r) {
+    const uint8_t* rec = uni(a.refs[r].record);
+    const uint64_t ref_bytes = uni(a.refs[r].bytes);
+    const int rti = uni(a.refs[r].table);
+    if (rti != ti) {
+      if (tid == 0 && first_block) set_status(a.status, CG_ERR_INVALID_ARG);
+      continue;
     }
-    if (__syncthreads_or(bt_bad)) {
-      if (tid == 0) set_status(a.status, CG_ERR_INVALID_ARG);
-      return;
+    if (ref_bytes < ds_expect || (reinterpret_cast<uintptr_t>(rec) & 15)) {
+      if (tid == 0) set_status(a.status, CG_ERR_CORRUPT);
+      continue;
     }
+    const uint32_t* rh = reinterpret_cast<const uint32_t*>(rec);
+    const int64_t c = uni(rh[2]);
+    const uint64_t rbytes = uni(*reinterpret_cast<const uint64_t*>(rec + 48));
+    const uint64_t dbytes = uni(*reinterpret_cast<const uint64_t*>(rec + 56));
+    bool bad = uni(rh[0]) != kRecordMagic || uni(rh[1]) != kVersion || c >= nch ||
+               (int32_t)uni(rh[3]) != a.level_id[ti];
+    if (!bad) {
+      bad = uni(*reinterpret_cast<const uint64_t*>(rec + 16)) != (uint64_t)(c * s.C) ||
+            uni(rh[6]) != (uint32_t)chunk_len(s.T, s.C, c) || uni(rh[7]) != (uint32_t)gpc ||
+            (int)uni(rh[8]) != s.L || (int)uni(rh[9]) != s.H || (int)uni(rh[10]) != s.D ||
+            uni(rh[11]) != ds_expect || rbytes > ref_bytes || ds_expect + dbytes > rbytes;
+    }
+    if (bad) {
+      if (tid == 0) set_status(a.status, CG_ERR_CORRUPT);
+      continue;
+    }
+    const int64_t n = chunk_len(s.T, s.C, c), t0 = c * s.C;
+    if (PAGED) {
+      bool bt_bad = false;
+      for (int64_t b = (t0 >> 4) + tid; b <= ((t0 + n - 1) >> 4); b += kDecThreads) {
+        const int32_t v = a.block_table[b];
+        bt_bad |= (v < 0 || (int64_t)v >= a.num_blocks);
+      }
+      if (__syncthreads_or(bt_bad)) {
+        if (tid == 0) set_status(a.status, CG_ERR_INVALID_ARG);
+        continue;
+      }
+    }
+    GroupRef& dst = nrec == 0 ? rr0 : nrec == 1 ? rr1 : rr2;
+    dst.rec = rec;
+    dst.ds = ds_expect;
+    dst.dbytes = dbytes;
+    dst.t0 = t0;
+    dst.n = (int)n;
+    ++nrec;
   }
+  if (nrec == 0) return;
+
   // the set's decoder tables, one contiguous 128 KB block
   const size_t set = (((size_t)g * 2 + kv) * s.H + h) * s.S + j;
   const uint4* dsrc = reinterpret_cast<const uint4*>(
       reinterpret_cast<const uint32_t*>(blob + tb_dec_offset(s.L, s.H, s.D, G)) + set * (kDecDwords * 64));
   for (int u = tid; u < kDecDwords * 64 / 4; u += kDecThreads) reinterpret_cast<uint4*>(tabs)[u] = dsrc[u];
-  __syncthreads();
+  const int lg_count = layers_in_group(blob, G, s.L, g, lane);
   const float step = blob_step(blob, g);
-  uint16_t* ring = rings + wave * kRingStride;
-  int cnt = 0;
-  for (int l = 0; l < s.L; ++l) {
-    if (layer_group(blob, G, l) != g) continue;
-    if ((cnt++ % kWaves) != wave) continue;
-    decode_group<PAGED>(a, tabs, ring, rec, ds_expect, dbytes, gpc, l, kv, h, j, t0, n, step, lane);
+  __syncthreads();
+
+  // items = (record, k-th layer of the group), record-major; wavefront w
+  // takes items w, w + 16, w + 32
+  const int items = nrec * lg_count;
+  const int mine = wave < items ? (items - 1 - wave) / kWaves + 1 : 0;
+  if (mine == 0) return;
+  Chain c[kChains];
+#pragma unroll
+  for (int k = 0; k < kChains; ++k) {
+    if (k < mine) {
+      const int it = wave + k * kWaves;
+      const int ri = it / lg_count;
+      GroupRef gr = ri == 0 ? rr0 : ri == 1 ? rr1 : rr2;
+      gr.l = layer_of_group(blob, G, s.L, g, it - ri * lg_count, lane);
+      chain_open<PAGED>(a, c[k], gr, gpc, kv, h, j, step, rings + (wave * kChains + k) * kRingStride,
+                        lane);
+    } else {
+      c[k].ok = false;
+    }
+  }
+  const bool all_ok = c[0].ok && (mine < 2 || c[1].ok) && (mine < 3 || c[2].ok);
+  if (all_ok && mine == 3) {
+    run_chains<PAGED, 3>(a, c, tabs, h, step, lane);
+  } else if (all_ok && mine == 2) {
+    run_chains<PAGED, 2>(a, c, tabs, h, step, lane);
+  } else {
+    // one chain, or a damaged directory entry among them: the rest one by one
+#pragma unroll
+    for (int k = 0; k < kChains; ++k)
+      if (c[k].ok) run_chains<PAGED, 1>(a, &c[k], tabs, h, step, lane);
   }
 }
 
@@ -1058,7 +1400,8 @@ hipError_t launch_write(const WriteArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, bool paged, hipStream_t st) {
-  const uint64_t blocks = (uint64_t)a.n_refs * a.g_max * 2 * a.s.H * a.s.S;
+  const uint64_t rblocks = (uint64_t)(a.n_refs + a.refs_per_block - 1) / a.refs_per_block;
+  const uint64_t blocks = rblocks * a.g_max * 2 * a.s.H * a.s.S;
   if (paged)
     hipLaunchKernelGGL(k_decode<true>, dim3((unsigned)blocks), dim3(kDecThreads), 0, st, a);
   else

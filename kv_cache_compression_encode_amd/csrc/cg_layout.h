@@ -38,10 +38,14 @@ constexpr int kDecDwords = 512;            // per channel
 constexpr int kDecBm = 0, kDecRb = 128 * 64, kDecInfo = 256 * 64;  // dword offsets in a set
 // Encoder set: [256 symbols][64] of f | b << 16. 64 KB.
 constexpr int kEncDwords = 256;            // per channel
-// Decoder ring per wavefront: 512 16-bit words refilled 256 at a time, plus a
-// 64-word mirror of words 0..63 so a read at (p mod 512) + k, k < 64, needs no wrap.
-constexpr int kRingWords = 512;
+// Decoder ring per chain: 256 16-bit words refilled 128 at a time (one dword
+// per lane), plus a 64-word mirror of words 0..63 so a read at
+// (p mod 256) + k, k < 64, needs no wrap.
+constexpr int kRingWords = 256;
 constexpr int kRingMirror = 64;
+constexpr int kRingBlock = 128;
+constexpr int kChains = 3;  // at most this many groups decoded together by one wavefront
+constexpr int kMaxRefsPerBlock = 3;  // records sharing one decode workgroup
 constexpr int kWaves = 16;  // wavefronts per workgroup of the codec kernels
 
 __host__ __device__ inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
@@ -178,6 +182,7 @@ struct DecodeArgs {
   Shape s;
   const cg_chunk_ref* refs;
   int32_t n_refs;
+  int32_t refs_per_block;  // records sharing one workgroup (same tables)
   int32_t n_tables;
   int32_t g_max;
   const uint8_t* tables[kMaxLevels];
