@@ -108,6 +108,14 @@ __device__ __forceinline__ int32_t quantize(uint16_t xh, float step, float rcp, 
   const float r = __builtin_rintf(v);
   sat += (r > 32767.0f) | (r < -32768.0f);
   nan_ += is_nan;
+  if (FAST) {
+    // the conversion instruction gives 0 for NaN and saturates +-Inf and
+    // out-of-range values, so one integer clamp finishes the job (k_qcheck
+    // compares this path with the exact one below on every fp16 input)
+    int32_t i;
+    asm("v_cvt_i32_f32 %0, %1" : "=v"(i) : "v"(r));
+    return i < -32768 ? -32768 : (i > 32767 ? 32767 : i);
+  }
   const float c = __builtin_fminf(__builtin_fmaxf(r, -32768.0f), 32767.0f);
   return is_nan ? 0 : (int32_t)c;
 }
@@ -160,8 +168,10 @@ __device__ __forceinline__ T* uni(T* p) {
 
 // Raw buffer resource over [base, base + bytes): accesses use a per-lane
 // offset in a VGPR plus a wave-uniform offset in an SGPR, so address
-// arithmetic stays on the scalar unit; loads past `bytes` return 0 and stores
-// past it are dropped by the hardware.
+// arithmetic stays on the scalar unit. The hardware range check covers the
+// VGPR offset (loads past `bytes` return 0, stores are dropped); offsets that
+// may run past the end therefore go in the VGPR, and the SGPR offset is used
+// only where the access is in bounds by construction.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
@@ -499,65 +509,91 @@ __global__ void __launch_bounds__(kNormThreads) k_norm(NormArgs a) {
 constexpr int kEncThreads = kWaves * 64;
 constexpr int kEncBatch = 16;
 
+// One token t >= 1 of a group, backward: symbol of q_t - q_{t-1}, escape
+// payload, renormalisation word, state update.
 template <bool FAST>
-__device__ __forceinline__ void encode_group(const uint16_t* __restrict__ xb, int64_t n, int D,
+__device__ __forceinline__ void encode_token(uint16_t xprev, int32_t& qhi, uint32_t& x, uint32_t& P,
                                              float step, float rcp, const uint32_t* ftab,
-                                             const double* rcp_tab, uint16_t* __restrict__ sb,
+                                             const double* rcp_tab, __amdgpu_buffer_rsrc_t sr,
+                                             uint32_t& fmin, int lane) {
+  uint32_t d0 = 0, d1 = 0;
+  const int32_t qlo = quantize<FAST>(xprev, step, rcp, d0, d1);
+  const uint32_t d16 = (uint32_t)(qhi - qlo);                      // low 16 bits: the wrapped delta
+  const uint32_t sraw = (uint32_t)((int32_t)(int16_t)d16 + 127);  // >= 255 (unsigned): escape
+  const uint32_t sym = sraw < 255u ? sraw : 255u;
+  const uint32_t e = ftab[sym * 64 + lane];
+  const uint32_t f = e & 0xFFFFu, bb = e >> 16;
+  fmin = f < fmin ? f : fmin;
+  const bool is_esc = sraw >= 255u;
+  const uint64_t me = __ballot(is_esc);
+  if (me) {
+    P -= (uint32_t)__popcll(me);
+    if (is_esc) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)d16, sr, 2u * mbcnt_base(me, 0), 2u * P, 0);
+  }
+  // renormalise when x >= f * 2^20, i.e. floor(x / 2^20) >= f (never for f = 4096)
+  const bool need = (x >> 20) >= f;
+  const uint64_t mr = __ballot(need);
+  P -= (uint32_t)__popcll(mr);
+  if (need) {
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)x, sr, 2u * mbcnt_base(mr, 0), 2u * P, 0);
+    x >>= 16;
+  }
+  // x <- floor(x/f)*4096 + x mod f + b = x + floor(x/f)*(4096-f) + b; the
+  // quotient is < 2^20 and 4096 - f < 2^12, so a 24-bit multiply is exact.
+  // (f = 0 only for a symbol missing from the table: the group is then
+  // invalid and CG_ERR_TABLE is reported; rcp_tab[0] = 0 keeps it finite)
+  const uint32_t qd = (uint32_t)((double)x * rcp_tab[f]);
+  x = x + __umul24(qd, kM - f) + bb;
+  qhi = qlo;
+}
+
+// Encodes tokens n-1 .. 1 of a group (backward), then the head. xr covers the
+// group's column of x (row t at byte t * row_bytes), sr its scratch slot of
+// cap words; every access is in bounds by construction.
+template <bool FAST>
+__device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, uint32_t row_bytes,
+                                             float step, float rcp, const uint32_t* ftab,
+                                             const double* rcp_tab, __amdgpu_buffer_rsrc_t sr,
                                              uint32_t cap, int lane, uint32_t& words,
                                              uint32_t& start, bool& table_err) {
+  const uint32_t lane2 = 2u * lane;
   uint32_t P = cap;
   uint32_t x = kL;
+  uint32_t fmin = 0xFFFFFFFFu;
   uint32_t d0 = 0, d1 = 0;
-  int32_t qhi = quantize<FAST>(xb[(size_t)(n - 1) * D], step, rcp, d0, d1);
-  bool terr = false;
-  for (int64_t i = n - 1; i >= 1; i -= kEncBatch) {
+  int32_t qhi = quantize<FAST>(
+      (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, (uint32_t)(n - 1) * row_bytes, 0), step,
+      rcp, d0, d1);
+  int i = n - 1;  // next token to encode
+  for (; i >= kEncBatch; i -= kEncBatch) {
+    uint16_t xv[kEncBatch];
+#pragma unroll
+    for (int k = 0; k < kEncBatch; ++k)
+      xv[k] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, (uint32_t)(i - 1 - k) * row_bytes, 0);
+#pragma unroll
+    for (int k = 0; k < kEncBatch; ++k)
+      encode_token<FAST>(xv[k], qhi, x, P, step, rcp, ftab, rcp_tab, sr, fmin, lane);
+  }
+  if (i >= 1) {  // the last i < 16 tokens
     uint16_t xv[kEncBatch];
 #pragma unroll
     for (int k = 0; k < kEncBatch; ++k) {
-      const int64_t row = i - 1 - k >= 0 ? i - 1 - k : 0;
-      xv[k] = xb[(size_t)row * D];
+      const int row = i - 1 - k >= 0 ? i - 1 - k : 0;
+      xv[k] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, uni((uint32_t)row * row_bytes), 0);
     }
 #pragma unroll
-    for (int k = 0; k < kEncBatch; ++k) {
-      if (i - k >= 1) {
-        const int32_t qlo = quantize<FAST>(xv[k], step, rcp, d0, d1);
-        const int32_t dlt = wrap16(qhi - qlo);
-        const uint32_t sym = symbol_of(dlt);
-        const uint32_t e = ftab[sym * 64 + lane];
-        const uint32_t f = e & 0xFFFFu, bb = e >> 16;
-        terr |= (f == 0);
-        const bool is_esc = sym == (uint32_t)kEsc;
-        const uint64_t me = __ballot(is_esc);
-        if (me) {
-          P -= (uint32_t)__popcll(me);
-          if (is_esc) sb[mbcnt_base(me, P)] = (uint16_t)(dlt & 0xFFFF);
-        }
-        // renormalise when x >= f * 2^20, i.e. x > (f << 20) - 1 (wraps to ~0 for f = 4096)
-        const bool need = x > ((f << 20) - 1u);
-        const uint64_t mr = __ballot(need);
-        P -= (uint32_t)__popcll(mr);
-        if (need) {
-          sb[mbcnt_base(mr, P)] = (uint16_t)(x & 0xFFFFu);
-          x >>= 16;
-        }
-        // x <- floor(x/f)*4096 + x mod f + b = x + floor(x/f)*(4096-f) + b
-        // (f = 0 only for a symbol missing from the table: the group is then
-        // invalid and CG_ERR_TABLE is reported; rcp_tab[0] = 0 keeps it finite)
-        const uint32_t qd = (uint32_t)((double)x * rcp_tab[f]);
-        x = x + qd * (kM - f) + bb;
-        qhi = qlo;
-      }
-    }
+    for (int k = 0; k < kEncBatch; ++k)
+      if (k < i) encode_token<FAST>(xv[k], qhi, x, P, step, rcp, ftab, rcp_tab, sr, fmin, lane);
   }
   P -= 64;
-  sb[P + lane] = (uint16_t)(qhi & 0xFFFF);
+  __builtin_amdgcn_raw_buffer_store_b16((uint16_t)qhi, sr, lane2, 2u * P, 0);
   P -= 64;
-  sb[P + lane] = (uint16_t)(x & 0xFFFFu);
+  __builtin_amdgcn_raw_buffer_store_b16((uint16_t)x, sr, lane2, 2u * P, 0);
   P -= 64;
-  sb[P + lane] = (uint16_t)(x >> 16);
+  __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(x >> 16), sr, lane2, 2u * P, 0);
   words = cap - P;
   start = P;
-  table_err |= terr;
+  table_err |= (fmin == 0);
 }
 
 __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
@@ -605,14 +641,17 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
     if ((cnt++ % kWaves) != wave) continue;
     const int64_t gi = (((int64_t)l * 2 + kv) * s.H + h) * s.S + j;
     const int64_t slot = cl * gpc + gi;
-    uint16_t* __restrict__ sb = a.scratch + (size_t)slot * a.cap_words;
-    const uint16_t* __restrict__ xb =
-        a.x + ((((size_t)l * 2 + kv) * s.H + h) * (size_t)s.T + t0) * s.D + 64 * j + lane;
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.scratch + (size_t)slot * a.cap_words, 2u * cap);
+    const uint16_t* xb = a.x + ((((size_t)l * 2 + kv) * s.H + h) * (size_t)s.T + t0) * s.D + 64 * j;
+    const uint32_t row_bytes = 2u * (uint32_t)s.D;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(xb, (uint32_t)n * row_bytes);
     uint32_t words, start;
     if (fast)
-      encode_group<true>(xb, n, s.D, step, rcp, ftab, rcp_tab, sb, cap, lane, words, start, table_err);
+      encode_group<true>(xr, (int)n, row_bytes, step, rcp, ftab, rcp_tab, sr, cap, lane, words, start,
+                         table_err);
     else
-      encode_group<false>(xb, n, s.D, step, rcp, ftab, rcp_tab, sb, cap, lane, words, start, table_err);
+      encode_group<false>(xr, (int)n, row_bytes, step, rcp, ftab, rcp_tab, sr, cap, lane, words, start,
+                          table_err);
     if (lane == 0) {
       a.group_words[slot] = words;
       a.group_start[slot] = start;
@@ -859,8 +898,10 @@ __device__ __forceinline__ void ring_put(Chain& c, uint32_t wbase, uint32_t v, i
   if (r < (uint32_t)kRingMirror) *reinterpret_cast<uint32_t*>(c.ring + kRingWords + r) = v;
 }
 
+// 128 words from word wbase on, one dword per lane; reads past the group's
+// padded extent (the prefetch runs ahead of the stream's end) return 0.
 __device__ __forceinline__ uint32_t stream_load(const Chain& c, uint32_t wbase, int lane) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(c.src, 4u * lane, 2u * wbase, 0);
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(c.src, 4u * lane + 2u * wbase, 0, 0);
 }
 
 // Sets up one group: checks its directory entry, stages its first 256 words,
