@@ -136,13 +136,12 @@ __device__ __forceinline__ uint16_t dequantize_low16(uint32_t q, float step) {
   return f2h(v);
 }
 
-__device__ __forceinline__ int32_t wrap16(int32_t v) { return ((v + 32768) & 0xFFFF) - 32768; }
-
-// d in [-127, 127] -> d + 127; anything else (as unsigned, >= 255) -> 255.
-__device__ __forceinline__ uint32_t symbol_of(int32_t d) {
-  const uint32_t u = (uint32_t)(d + 127);
-  return u < (uint32_t)kEsc ? u : (uint32_t)kEsc;
+// 127 + wrap16(q_t - q_{t-1}) as unsigned: below 255 it is the symbol,
+// otherwise the delta needs an escape (symbol 255).
+__device__ __forceinline__ uint32_t sym_raw(int32_t q_t, int32_t q_prev) {
+  return (uint32_t)((int32_t)(int16_t)(uint32_t)(q_t - q_prev) + 127);
 }
+
 
 // mbcnt with a base: base + number of set bits of m in lanes below this one.
 __device__ __forceinline__ uint32_t mbcnt_base(uint64_t m, uint32_t base) {
@@ -304,37 +303,56 @@ constexpr int kHistThreads = 512;
 constexpr int kHistWaves = kHistThreads / 64;
 constexpr int kHistBatch = 16;
 
-template <bool FAST>
-__device__ __forceinline__ void hist_range(const uint16_t* __restrict__ xb, int64_t t_begin,
-                                           int64_t t_end, int C, int D, float step, float rcp,
-                                           uint32_t* hist, int lane, uint32_t& elems,
-                                           uint32_t& sat, uint32_t& nan_, uint32_t& esc) {
+// Tokens [t_begin, t_end) of one (layer, K|V, head, slice) column; xr
+// covers the column from token 0 (row t at byte t * row_bytes). Every load
+// is in bounds by construction. STATS adds the saturated / NaN counts.
+template <bool FAST, bool STATS>
+__device__ __forceinline__ void hist_range(__amdgpu_buffer_rsrc_t xr, uint32_t row_bytes, int t_begin,
+                                           int t_end, int C, float step, float rcp, uint32_t* hist,
+                                           int lane, uint32_t& sat, uint32_t& nan_) {
+  const uint32_t lane2 = 2u * lane;
+  uint32_t* hl = hist + lane;
   int32_t prev = 0;
-  int pos = (int)(t_begin % C);  // position of t_begin inside its chunk
+  int pos = t_begin % C;  // position of the next token inside its chunk
   if (pos != 0) {
     uint32_t d0 = 0, d1 = 0;
-    prev = quantize<FAST>(xb[(size_t)(t_begin - 1) * D], step, rcp, d0, d1);
+    prev = quantize<FAST>(
+        (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, (uint32_t)(t_begin - 1) * row_bytes, 0),
+        step, rcp, d0, d1);
   }
-  for (int64_t t = t_begin; t < t_end; t += kHistBatch) {
+  auto one = [&](uint16_t xh) {
+    uint32_t s0 = 0, n0 = 0;
+    const int32_t q = quantize<FAST>(xh, step, rcp, s0, n0);
+    if (STATS) {
+      sat += s0;
+      nan_ += n0;
+    }
+    const uint32_t r = sym_raw(q, prev);
+    const uint32_t sym = pos != 0 ? (r < 255u ? r : 255u) : 256u;  // row 256: chunk heads
+    atomicAdd(hl + sym * 64, 1u);
+    prev = q;
+    pos = (pos + 1 == C) ? 0 : pos + 1;
+  };
+  int t = t_begin;
+  for (; t + kHistBatch <= t_end; t += kHistBatch) {
+    uint16_t xv[kHistBatch];
+#pragma unroll
+    for (int k = 0; k < kHistBatch; ++k)
+      xv[k] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, (uint32_t)(t + k) * row_bytes, 0);
+#pragma unroll
+    for (int k = 0; k < kHistBatch; ++k) one(xv[k]);
+  }
+  if (t < t_end) {
     uint16_t xv[kHistBatch];
 #pragma unroll
     for (int k = 0; k < kHistBatch; ++k) {
-      const int64_t tk = t + k < t_end ? t + k : t_end - 1;
-      xv[k] = xb[(size_t)tk * D];
+      const int tk = t + k < t_end ? t + k : t_end - 1;
+      xv[k] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, uni((uint32_t)tk * row_bytes), 0);
     }
 #pragma unroll
-    for (int k = 0; k < kHistBatch; ++k) {
-      if (t + k < t_end) {
-        const int32_t q = quantize<FAST>(xv[k], step, rcp, sat, nan_);
-        const uint32_t sym = pos != 0 ? symbol_of(wrap16(q - prev)) : 256u;
-        atomicAdd(&hist[sym * 64 + lane], 1u);
-        esc += (sym == (uint32_t)kEsc);
-        prev = q;
-        pos = (pos + 1 == C) ? 0 : pos + 1;
-      }
-    }
+    for (int k = 0; k < kHistBatch; ++k)
+      if (t + k < t_end) one(xv[k]);
   }
-  elems += (uint32_t)(t_end - t_begin);
 }
 
 __global__ void __launch_bounds__(kHistThreads) k_hist(HistArgs a) {
@@ -357,15 +375,23 @@ __global__ void __launch_bounds__(kHistThreads) k_hist(HistArgs a) {
   const bool fast = qflag(a.blob, s.L, s.H, s.D, G, g);
   __syncthreads();
 
-  const uint16_t* __restrict__ xb =
-      a.x + (((size_t)l * 2 + kv) * s.H + h) * (size_t)s.T * s.D + 64 * j + lane;
-  const int64_t t_begin = s.T * wave / kHistWaves, t_end = s.T * (wave + 1) / kHistWaves;
-  uint32_t sat = 0, nan_ = 0, esc = 0, elems = 0;
+  const uint16_t* xb = a.x + (((size_t)l * 2 + kv) * s.H + h) * (size_t)s.T * s.D + 64 * j;
+  const uint32_t row_bytes = 2u * (uint32_t)s.D;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(xb, (uint32_t)(s.T * row_bytes));
+  const int t_begin = (int)(s.T * wave / kHistWaves), t_end = (int)(s.T * (wave + 1) / kHistWaves);
+  uint32_t sat = 0, nan_ = 0;
   if (t_begin < t_end) {
-    if (fast)
-      hist_range<true>(xb, t_begin, t_end, s.C, s.D, step, rcp, hist, lane, elems, sat, nan_, esc);
-    else
-      hist_range<false>(xb, t_begin, t_end, s.C, s.D, step, rcp, hist, lane, elems, sat, nan_, esc);
+    if (a.stats) {
+      if (fast)
+        hist_range<true, true>(xr, row_bytes, t_begin, t_end, s.C, step, rcp, hist, lane, sat, nan_);
+      else
+        hist_range<false, true>(xr, row_bytes, t_begin, t_end, s.C, step, rcp, hist, lane, sat, nan_);
+    } else {
+      if (fast)
+        hist_range<true, false>(xr, row_bytes, t_begin, t_end, s.C, step, rcp, hist, lane, sat, nan_);
+      else
+        hist_range<false, false>(xr, row_bytes, t_begin, t_end, s.C, step, rcp, hist, lane, sat, nan_);
+    }
   }
   __syncthreads();
   const size_t set = (((size_t)g * 2 + kv) * s.H + h) * s.S + j;
@@ -375,9 +401,11 @@ __global__ void __launch_bounds__(kHistThreads) k_hist(HistArgs a) {
     if (c) atomicAdd(&counts[i], c);
   }
   if (a.stats) {
-    const uint32_t e = wave_sum(elems), st = wave_sum(sat), nn = wave_sum(nan_), es = wave_sum(esc);
+    // escapes are the histogram's row 255, counted once per workgroup
+    const uint32_t st = wave_sum(sat), nn = wave_sum(nan_);
+    const uint32_t es = wave == 0 ? wave_sum(hist[255 * 64 + lane]) : 0u;
     if (lane == 0) {
-      atomicAdd(&a.stats[0], (unsigned long long)e);
+      if (wave == 0) atomicAdd(&a.stats[0], (unsigned long long)(64 * s.T));
       if (st) atomicAdd(&a.stats[1], (unsigned long long)st);
       if (nn) atomicAdd(&a.stats[2], (unsigned long long)nn);
       if (es) atomicAdd(&a.stats[3], (unsigned long long)es);
@@ -518,8 +546,8 @@ __device__ __forceinline__ void encode_token(uint16_t xprev, int32_t& qhi, uint3
                                              uint32_t& fmin, int lane) {
   uint32_t d0 = 0, d1 = 0;
   const int32_t qlo = quantize<FAST>(xprev, step, rcp, d0, d1);
-  const uint32_t d16 = (uint32_t)(qhi - qlo);                      // low 16 bits: the wrapped delta
-  const uint32_t sraw = (uint32_t)((int32_t)(int16_t)d16 + 127);  // >= 255 (unsigned): escape
+  const uint32_t d16 = (uint32_t)(qhi - qlo);  // low 16 bits: the wrapped delta
+  const uint32_t sraw = sym_raw(qhi, qlo);
   const uint32_t sym = sraw < 255u ? sraw : 255u;
   const uint32_t e = ftab[sym * 64 + lane];
   const uint32_t f = e & 0xFFFFu, bb = e >> 16;
