@@ -231,7 +231,7 @@ cg_status cg_encode(const cg_shape* shape, const cg_level* level, const void* ta
   const int G = level->n_groups;
   const int64_t gpc = groups_per_chunk(s.L, s.H, s.D);
   if ((uint64_t)n * G * 2 * s.H * s.S >= (1ull << 31) || cap >= (1ull << 32)) return CG_ERR_UNSUPPORTED;
-  const int gpb = 16;  // groups per copy block
+  const int gpb = 4;  // groups per copy block (one per wavefront)
   if ((uint64_t)n * (1 + (gpc + gpb - 1) / gpb) >= (1ull << 31)) return CG_ERR_UNSUPPORTED;
 
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);

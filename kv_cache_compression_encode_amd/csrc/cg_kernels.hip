@@ -753,6 +753,69 @@ __global__ void __launch_bounds__(kScanThreads) k_chunk_scan(ChunkScanArgs a) {
 // wavefront per group) from the scratch slots into place.
 // ---------------------------------------------------------------------------
 constexpr int kWriteThreads = 256;
+constexpr int kCopyUnroll = 4;
+typedef unsigned int v4u32_t __attribute__((ext_vector_type(4)));
+
+// 16 output bytes from the 32 source bytes lo|hi, starting Q dwords plus
+// bs bytes into lo.
+template <int Q>
+__device__ __forceinline__ uint4 shift_pick(const uint4& lo, const uint4& hi, uint32_t bs) {
+  const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  return make_uint4(__builtin_amdgcn_alignbyte(w[Q + 1], w[Q + 0], bs),
+                    __builtin_amdgcn_alignbyte(w[Q + 2], w[Q + 1], bs),
+                    __builtin_amdgcn_alignbyte(w[Q + 3], w[Q + 2], bs),
+                    __builtin_amdgcn_alignbyte(w[Q + 4], w[Q + 3], bs));
+}
+
+// Zero the bytes of a 16-byte output chunk at or past `end` (byte offset o
+// of the chunk); the stream ends on a 2-byte boundary.
+__device__ __forceinline__ uint32_t keep_below(uint32_t v, uint32_t o, uint32_t end) {
+  return o + 4 <= end ? v : (o + 2 <= end ? (v & 0xFFFFu) : 0u);
+}
+
+// One wavefront copies words [P, P + nw) of a scratch slot (src, 16-byte
+// aligned) to dst as 16-byte chunks, zero-padded to nbytes (a multiple of
+// 16). Source reads past the slot return 0 (range-checked VGPR offsets).
+template <int Q>
+__device__ __forceinline__ void copy_stream_q(__amdgpu_buffer_rsrc_t src, uint32_t a0, uint32_t bs,
+                                              uint32_t end, __amdgpu_buffer_rsrc_t dst, uint32_t nbytes,
+                                              int lane) {
+  for (uint32_t base = 0; base < nbytes; base += 64 * 16 * kCopyUnroll) {
+    uint4 lo[kCopyUnroll], hi[kCopyUnroll];
+#pragma unroll
+    for (int k = 0; k < kCopyUnroll; ++k) {
+      const uint32_t off = base + 16u * (64u * k + lane);
+      lo[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(src, a0 + off, 0, 0));
+      hi[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(src, a0 + off + 16, 0, 0));
+    }
+#pragma unroll
+    for (int k = 0; k < kCopyUnroll; ++k) {
+      const uint32_t off = base + 16u * (64u * k + lane);
+      if (off < nbytes) {
+        uint4 v = shift_pick<Q>(lo[k], hi[k], bs);
+        if (off + 16 > end) {
+          v.x = keep_below(v.x, off, end);
+          v.y = keep_below(v.y, off + 4, end);
+          v.z = keep_below(v.z, off + 8, end);
+          v.w = keep_below(v.w, off + 12, end);
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, v), dst, off, 0, 0);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void copy_stream(__amdgpu_buffer_rsrc_t src, uint32_t P, uint32_t nw,
+                                            __amdgpu_buffer_rsrc_t dst, uint32_t nbytes, int lane) {
+  const uint32_t sb = 2u * P, a0 = sb & ~15u, q = (sb & 15u) >> 2, bs = sb & 3u, end = 2u * nw;
+  switch (q) {
+    case 0: copy_stream_q<0>(src, a0, bs, end, dst, nbytes, lane); break;
+    case 1: copy_stream_q<1>(src, a0, bs, end, dst, nbytes, lane); break;
+    case 2: copy_stream_q<2>(src, a0, bs, end, dst, nbytes, lane); break;
+    default: copy_stream_q<3>(src, a0, bs, end, dst, nbytes, lane); break;
+  }
+}
+
 
 __global__ void __launch_bounds__(kWriteThreads) k_write(WriteArgs a) {
   if (uni(a.chunk_offsets[a.n_chunks]) > a.out_cap) return;
@@ -798,32 +861,10 @@ __global__ void __launch_bounds__(kWriteThreads) k_write(WriteArgs a) {
     const int64_t slot = cl * a.gpc + gi;
     const uint32_t nw = uni(a.group_words[slot]);
     const uint32_t P = uni(a.group_start[slot]);
-    // the slot is 16-byte aligned; the stream is words [P, P + nw) of it
-    const uint32_t* __restrict__ s32 =
-        reinterpret_cast<const uint32_t*>(a.scratch + (size_t)slot * a.cap_words);
     const uint64_t g0 = uni(go[gi]), g1 = uni(go[gi + 1]);
-    uint32_t* __restrict__ dst = reinterpret_cast<uint32_t*>(rec + ds + g0);
-    const uint32_t ndw = (uint32_t)((g1 - g0) / 4);
-    const uint32_t base = P >> 1;
-    if ((P & 1) == 0) {
-      for (uint32_t k = lane; k < ndw; k += 64) {
-        uint32_t w = 0;
-        if (2 * k + 1 < nw) {
-          w = s32[base + k];
-        } else if (2 * k < nw) {
-          w = s32[base + k] & 0xFFFFu;
-        }
-        dst[k] = w;
-      }
-    } else {
-      // word 2k of the stream is the high half of dword base+k
-      for (uint32_t k = lane; k < ndw; k += 64) {
-        uint32_t w = 0;
-        if (2 * k < nw) w = s32[base + k] >> 16;
-        if (2 * k + 1 < nw) w |= s32[base + k + 1] << 16;
-        dst[k] = w;
-      }
-    }
+    const __amdgpu_buffer_rsrc_t src = make_rsrc(a.scratch + (size_t)slot * a.cap_words, 2u * (uint32_t)a.cap_words);
+    const __amdgpu_buffer_rsrc_t dst = make_rsrc(rec + ds + g0, (uint32_t)(g1 - g0));
+    copy_stream(src, P, nw, dst, (uint32_t)(g1 - g0), lane);
   }
 }
 
