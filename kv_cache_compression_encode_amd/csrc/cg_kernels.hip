@@ -930,6 +930,7 @@ struct Chain {
   // values carried between the phases of one token (pipelined loop)
   uint32_t above, rankx, info, w;
   uint64_t mr;
+  int pref_it;  // pipelined loop: iteration that issued the load now in pref
 };
 
 struct GroupRef {
@@ -1135,11 +1136,47 @@ __device__ __forceinline__ void chain_steps(const DecodeArgs& a, Chain* c, int i
 // one phase of every chain, so each LDS read is covered by a full slot of the
 // other chains' work instead of being waited for at once.
 
-__device__ __forceinline__ void ph_a(Chain& c, const uint32_t* tabs, int lane) {
+// Waits for the stream load issued `age` pipelined iterations ago. Every
+// iteration of an NC-chain loop issues NC stores, and a chain stores its
+// token right before its refill, so at least NC * (age - 1) + 1 vector-memory
+// operations were issued after that load; vector-memory operations complete
+// in order, so waiting until no more than that many are outstanding suffices
+// and stores issued since then need not drain.
+template <int NC>
+__device__ __forceinline__ void wait_stream_load(int age) {
+  if (age >= 4) {
+    if (NC == 3) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+  } else if (age >= 2) {
+    if (NC == 3) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+  }
+}
+
+// The next 128-word block into a register. Issued as inline assembly so the
+// compiler does not track it (it would wait at the consumer for every store
+// issued since, assuming the load could be the most recent one); the
+// consumer waits with wait_stream_load instead, and chain_pipe retires all
+// such loads before it returns.
+__device__ __forceinline__ uint32_t stream_load_async(const Chain& c, uint32_t wbase, int lane) {
+  uint32_t v;
+  asm volatile("buffer_load_dword %0, %1, %2, 0 offen"
+               : "=&v"(v)
+               : "v"(4u * lane + 2u * wbase), "s"(c.src)
+               : "memory");
+  return v;
+}
+
+template <int NC>
+__device__ __forceinline__ void ph_a(Chain& c, const uint32_t* tabs, int lane, int it) {
   if (c.loaded - c.p < (uint32_t)kRingBlock) {
+    wait_stream_load<NC>(it - c.pref_it);
     ring_put(c, c.loaded, c.pref, lane);
     c.loaded += kRingBlock;
-    c.pref = stream_load(c, c.loaded, lane);
+    c.pref = stream_load_async(c, c.loaded, lane);
+    c.pref_it = it;
     __builtin_amdgcn_wave_barrier();
   }
   const uint32_t ob = ((c.x << 3) & 0x7F00u) | (4u * lane);  // word (slot >> 5) of this lane
@@ -1191,26 +1228,31 @@ __device__ __forceinline__ void chain_pipe(const DecodeArgs& a, Chain* c, int i0
                                            const uint32_t* tabs, int h, float step, int lane) {
   static_assert(NC == 2 || NC == 3, "two or three chains");
   const uint32_t row_bytes = 2u * (uint32_t)a.s.D;
-  // see chain_steps: no load of an earlier loop may stay pending
+  // see chain_steps: no load of an earlier loop may stay pending; the
+  // compiler-issued prefetch of chain_open is complete after this wait
   __builtin_amdgcn_s_waitcnt(0x0F70);
-  // prologue: chain 0 runs A, B, C of token i0; chain 1 A, B; chain 2 A
-  ph_a(c[0], tabs, lane);
+#pragma unroll
+  for (int k = 0; k < NC; ++k) c[k].pref_it = -8;
+  // prologue (iteration 0): chain 0 runs A, B, C of token i0; chain 1 A, B;
+  // chain 2 A
+  ph_a<NC>(c[0], tabs, lane, 0);
   CG_SLOT;
   ph_b(c[0], tabs);
   CG_SLOT;
-  ph_a(c[1], tabs, lane);
+  ph_a<NC>(c[1], tabs, lane, 0);
   CG_SLOT;
   ph_c(c[0]);
   CG_SLOT;
   ph_b(c[1], tabs);
   CG_SLOT;
   if (NC == 3) {
-    ph_a(c[2], tabs, lane);
+    ph_a<NC>(c[2], tabs, lane, 0);
     CG_SLOT;
   }
-  for (int i = i0; i < i1 - 1; ++i) {
+  int it = 1;
+  for (int i = i0; i < i1 - 1; ++i, ++it) {
     ph_d<PAGED>(a, c[0], i, h, step, row_bytes, lane);
-    ph_a(c[0], tabs, lane);
+    ph_a<NC>(c[0], tabs, lane, it);
     CG_SLOT;
     ph_c(c[1]);
     CG_SLOT;
@@ -1221,7 +1263,7 @@ __device__ __forceinline__ void chain_pipe(const DecodeArgs& a, Chain* c, int i0
     ph_b(c[0], tabs);
     CG_SLOT;
     ph_d<PAGED>(a, c[1], i, h, step, row_bytes, lane);
-    ph_a(c[1], tabs, lane);
+    ph_a<NC>(c[1], tabs, lane, it);
     CG_SLOT;
     if (NC == 3) {
       ph_c(c[2]);
@@ -1233,7 +1275,7 @@ __device__ __forceinline__ void chain_pipe(const DecodeArgs& a, Chain* c, int i0
     CG_SLOT;
     if (NC == 3) {
       ph_d<PAGED>(a, c[2], i, h, step, row_bytes, lane);
-      ph_a(c[2], tabs, lane);
+      ph_a<NC>(c[2], tabs, lane, it);
       CG_SLOT;
     }
   }
@@ -1246,6 +1288,9 @@ __device__ __forceinline__ void chain_pipe(const DecodeArgs& a, Chain* c, int i0
     ph_c(c[2]);
     ph_d<PAGED>(a, c[2], i1 - 1, h, step, row_bytes, lane);
   }
+  // the last prefetches may still be in flight into registers the compiler
+  // considers free from here on
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // The k-th layer (0-based, ascending) of layer group g, or -1; computed by
