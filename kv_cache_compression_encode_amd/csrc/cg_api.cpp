@@ -6,6 +6,9 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <algorithm>
+#include <functional>
+#include <vector>
 
 #include "cg_layout.h"
 
@@ -305,36 +308,84 @@ static int compute_units() {
   return cus;
 }
 
-// Records per decode workgroup when every record uses one table set. A
-// workgroup holds R records x (layers of its group) groups, dealt to its 16
-// wavefronts, so a wavefront runs c = ceil(items / 16) <= 3 interleaved
-// chains. One workgroup fits a compute unit (its tables fill the LDS), so
-// the decode takes about ceil(workgroups / CUs) rounds, each as long as a
-// wavefront's c-chain step. Relative step times (1 chain = 100) are measured
-// on gfx950; the R with the least rounds x step time wins.
-static int refs_per_block(const Shape& s, const cg_level& lv, int32_t n_refs) {
-  static const int kStepCost[kChains + 1] = {0, 100, 168, 215};
+// Decode work plan when every record uses one table set. A workgroup holds
+// R records x (layers of its group) groups, dealt to its 16 wavefronts, so a
+// wavefront runs c = ceil(items / 16) <= 3 interleaved chains. One workgroup
+// fits a compute unit (its tables fill the LDS). Records [0, split) go in
+// blocks of R1 and the rest in blocks of R2; the plan with the shortest
+// simulated greedy dispatch (workgroups taken in launch order by the first
+// free compute unit) wins. Records are taken as full chunks, except that a
+// decode of as many records as the sequence has chunks is taken to end with
+// the sequence's last, shorter chunk (the plan only affects speed).
+// Workgroup times per chain count are measured on gfx950 (3 chains = 1000).
+static void plan_decode(const Shape& s, const cg_level& lv, int32_t n_refs, DecodeArgs* a) {
+  static const int kWgCost[kChains + 1] = {0, 380, 710, 1000};
+  static const int kWgFixed = 5;  // table load and set-up
   int lg_max = 0;
   for (int g = 0; g < lv.n_groups; ++g) {
     int n = 0;
     for (int l = 0; l < s.L; ++l) n += lv.layer_group[l] == g;
     if (n > lg_max) lg_max = n;
   }
-  const uint64_t sets = (uint64_t)lv.n_groups * 2 * s.H * s.S;
-  const uint64_t cus = (uint64_t)compute_units();
-  int best = 1;
-  uint64_t best_cost = ~0ull;
-  for (int r = 1; r <= kMaxRefsPerBlock && r <= n_refs; ++r) {
-    const int chains = (r * lg_max + kWaves - 1) / kWaves;
-    if (chains > kChains) break;
-    const uint64_t wgs = (uint64_t)((n_refs + r - 1) / r) * sets;
-    const uint64_t cost = (wgs + cus - 1) / cus * (uint64_t)kStepCost[chains < 1 ? 1 : chains];
-    if (cost < best_cost) {
-      best_cost = cost;
-      best = r;
+  const int64_t sets = (int64_t)lv.n_groups * 2 * s.H * s.S;
+  const int cus = compute_units();
+  auto chains = [&](int r) { return (r * lg_max + kWaves - 1) / kWaves; };
+  auto cost = [&](int r) { return (int64_t)kWgCost[chains(r)] + kWgFixed; };
+  // length of the last record in units of 1/1024 chunk
+  const int64_t nch = n_chunks(s.T, s.C);
+  const int64_t last = n_refs == nch ? chunk_len(s.T, s.C, nch - 1) * 1024 / s.C : 1024;
+  // a block of r records whose last one is `last` long: all chains for that
+  // length, then one chain fewer for the rest
+  auto cost_last = [&](int r) {
+    const int64_t full = r > 1 ? kWgCost[chains(r - 1)] : 0;
+    return (int64_t)kWgCost[chains(r)] * last / 1024 + full * (1024 - last) / 1024 + kWgFixed;
+  };
+  a->refs_per_block = 1;
+  a->split = 0;
+  a->refs_per_block2 = 1;
+  int64_t best = INT64_MAX;
+  std::vector<int64_t> heap;
+  for (int r1 = 1; r1 <= kMaxRefsPerBlock && r1 <= n_refs && chains(r1) <= kChains; ++r1) {
+    for (int r2 = 1; r2 <= r1; ++r2) {
+      for (int split = 0; split <= n_refs; split += r1) {
+        if (split == n_refs && r2 != 1) continue;  // no second class
+        const int64_t n1 = split / r1, n2 = (n_refs - split + r2 - 1) / r2;
+        int64_t span;
+        if ((n1 + n2) * sets > 200000) {
+          // too many workgroups to simulate: whole rounds
+          const int64_t w1 = n1 * sets, w2 = n2 * sets;
+          span = (w1 + w2 + cus - 1) / cus * (w1 ? cost(r1) : cost(r2));
+        } else {
+          heap.assign(cus, 0);
+          std::make_heap(heap.begin(), heap.end(), std::greater<int64_t>());
+          auto run = [&](int64_t jobs, int64_t t) {
+            for (int64_t k = 0; k < jobs; ++k) {
+              std::pop_heap(heap.begin(), heap.end(), std::greater<int64_t>());
+              heap.back() += t;
+              std::push_heap(heap.begin(), heap.end(), std::greater<int64_t>());
+            }
+          };
+          if (n2 == 0) {
+            run((n1 - 1) * sets, cost(r1));
+            run(sets, cost_last(r1));
+          } else {
+            run(n1 * sets, cost(r1));
+            // the last block holds the last record and may hold fewer records
+            const int64_t rem = (n_refs - split) % r2;
+            run((n2 - 1) * sets, cost(r2));
+            run(sets, cost_last(rem ? (int)rem : r2));
+          }
+          span = *std::max_element(heap.begin(), heap.end());
+        }
+        if (span < best) {
+          best = span;
+          a->refs_per_block = r1;
+          a->split = split;
+          a->refs_per_block2 = r2;
+        }
+      }
     }
   }
-  return best;
 }
 
 static cg_status decode_common(const cg_shape* shape, int32_t n_levels, const cg_level* levels,
@@ -363,7 +414,13 @@ static cg_status decode_common(const cg_shape* shape, int32_t n_levels, const cg
   a->s = s;
   a->refs = refs_dev;
   a->n_refs = n_refs;
-  a->refs_per_block = n_levels == 1 ? refs_per_block(s, levels[0], n_refs) : 1;
+  if (n_levels == 1) {
+    plan_decode(s, levels[0], n_refs, a);
+  } else {
+    a->refs_per_block = 1;
+    a->split = 0;
+    a->refs_per_block2 = 1;
+  }
   a->n_tables = n_levels;
   a->g_max = g_max;
   a->status = status_dev;
@@ -467,6 +524,9 @@ cg_status cg_stream_decode_paged(const cg_shape* shape, int32_t n_levels, const 
     if (e == hipSuccess) {
       a.refs = refs_dev + slot;
       a.n_refs = 1;
+      a.refs_per_block = 1;
+      a.split = 0;
+      a.refs_per_block2 = 1;
       e = launch_decode(a, true, stream);
     }
     if (e == hipSuccess) e = hipEventRecord(consumed[slot], stream);

@@ -1171,7 +1171,7 @@ __device__ __forceinline__ uint32_t stream_load_async(const Chain& c, uint32_t w
 
 template <int NC>
 __device__ __forceinline__ void ph_a(Chain& c, const uint32_t* tabs, int lane, int it) {
-  if (c.loaded - c.p < (uint32_t)kRingBlock) {
+  if (c.p > c.loaded - (uint32_t)kRingBlock) {  // fewer than 128 words staged (loaded >= 256)
     wait_stream_load<NC>(it - c.pref_it);
     ring_put(c, c.loaded, c.pref, lane);
     c.loaded += kRingBlock;
@@ -1357,8 +1357,15 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
   bid /= 2;
   const int g = (int)(bid % a.g_max);
   const int64_t rb = bid / a.g_max;
-  const int64_t r_begin = rb * a.refs_per_block;
-  const int64_t r_end = r_begin + a.refs_per_block < a.n_refs ? r_begin + a.refs_per_block : a.n_refs;
+  const int64_t nb1 = a.split / a.refs_per_block;
+  int64_t r_begin, r_end;
+  if (rb < nb1) {
+    r_begin = rb * a.refs_per_block;
+    r_end = r_begin + a.refs_per_block;
+  } else {
+    r_begin = a.split + (rb - nb1) * a.refs_per_block2;
+    r_end = r_begin + a.refs_per_block2 < a.n_refs ? r_begin + a.refs_per_block2 : a.n_refs;
+  }
   const bool first_block = (g == 0 && kv == 0 && h == 0 && j == 0);
 
   // all records of a workgroup use the first one's table set
@@ -1555,7 +1562,8 @@ hipError_t launch_write(const WriteArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, bool paged, hipStream_t st) {
-  const uint64_t rblocks = (uint64_t)(a.n_refs + a.refs_per_block - 1) / a.refs_per_block;
+  const uint64_t rblocks = (uint64_t)(a.split / a.refs_per_block) +
+                           (uint64_t)(a.n_refs - a.split + a.refs_per_block2 - 1) / a.refs_per_block2;
   const uint64_t blocks = rblocks * a.g_max * 2 * a.s.H * a.s.S;
   if (paged)
     hipLaunchKernelGGL(k_decode<true>, dim3((unsigned)blocks), dim3(kDecThreads), 0, st, a);

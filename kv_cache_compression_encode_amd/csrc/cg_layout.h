@@ -182,7 +182,12 @@ struct DecodeArgs {
   Shape s;
   const cg_chunk_ref* refs;
   int32_t n_refs;
-  int32_t refs_per_block;  // records sharing one workgroup (same tables)
+  // Records [0, split) go to workgroups in blocks of refs_per_block, the
+  // rest in blocks of refs_per_block2 (all of a workgroup's records share
+  // one table set); first-class blocks come first in launch order.
+  int32_t refs_per_block;
+  int32_t split;
+  int32_t refs_per_block2;
   int32_t n_tables;
   int32_t g_max;
   const uint8_t* tables[kMaxLevels];
