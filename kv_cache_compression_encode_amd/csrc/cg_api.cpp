@@ -94,6 +94,133 @@ cg_status check_range(const Shape& s, int64_t cb, int64_t ce) {
 
 }  // namespace
 
+static int compute_units() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return 256;
+  return cus;
+}
+
+// Splits n_rec records (decode) or chunks (encode) of each of `sets` table
+// sets into workgroups: records [0, split) in blocks of r1, the rest in
+// blocks of r2, first-class blocks launched first. One workgroup fits a
+// compute unit (its tables fill the LDS). The plan with the shortest
+// simulated greedy dispatch (workgroups taken in launch order by the first
+// free compute unit) wins. cost(r, last) is a workgroup's time for a block
+// of r records, the last of which is `last` / 1024 of a full one.
+struct BlockPlan {
+  int r1 = 1, split = 0, r2 = 1;
+};
+
+template <class Cost>
+static BlockPlan plan_blocks(int64_t n_rec, int64_t sets, int max_r, int64_t last, Cost cost) {
+  const int cus = compute_units();
+  BlockPlan best;
+  int64_t best_span = INT64_MAX;
+  std::vector<int64_t> heap;
+  for (int r1 = 1; r1 <= max_r && r1 <= n_rec; ++r1) {
+    for (int r2 = 1; r2 <= r1; ++r2) {
+      for (int64_t split = 0; split <= n_rec; split += r1) {
+        if (split == n_rec && r2 != 1) continue;  // no second class
+        const int64_t n1 = split / r1, n2 = (n_rec - split + r2 - 1) / r2;
+        const int64_t rem = (n_rec - split) % r2;
+        int64_t span;
+        if ((n1 + n2) * sets > 200000) {
+          // too many workgroups to simulate: whole rounds
+          const int64_t w = (n1 + n2) * sets;
+          span = (w + cus - 1) / cus * cost(n1 ? r1 : r2, 1024);
+        } else {
+          heap.assign(cus, 0);
+          auto run = [&](int64_t jobs, int64_t t) {
+            for (int64_t k = 0; k < jobs; ++k) {
+              std::pop_heap(heap.begin(), heap.end(), std::greater<int64_t>());
+              heap.back() += t;
+              std::push_heap(heap.begin(), heap.end(), std::greater<int64_t>());
+            }
+          };
+          if (n2 == 0) {
+            run((n1 - 1) * sets, cost(r1, 1024));
+            run(sets, cost(r1, last));
+          } else {
+            run(n1 * sets, cost(r1, 1024));
+            run((n2 - 1) * sets, cost(r2, 1024));
+            run(sets, cost(rem ? (int)rem : r2, last));  // the block with the last record
+          }
+          span = *std::max_element(heap.begin(), heap.end());
+        }
+        if (span < best_span) {
+          best_span = span;
+          best.r1 = r1;
+          best.split = (int)split;
+          best.r2 = r2;
+        }
+      }
+    }
+  }
+  return best;
+}
+
+static int max_layers_per_group(const Shape& s, const cg_level& lv) {
+  int lg_max = 0;
+  for (int g = 0; g < lv.n_groups; ++g) {
+    int n = 0;
+    for (int l = 0; l < s.L; ++l) n += lv.layer_group[l] == g;
+    if (n > lg_max) lg_max = n;
+  }
+  return lg_max;
+}
+
+// length of the last of n records in 1/1024 chunk: a call covering the
+// sequence's last chunk is taken to end with it (the plan only affects speed)
+static int64_t last_len(const Shape& s, bool ends_at_last_chunk) {
+  const int64_t nch = n_chunks(s.T, s.C);
+  return ends_at_last_chunk ? chunk_len(s.T, s.C, nch - 1) * 1024 / s.C : 1024;
+}
+
+// Decode: a workgroup holds R records x (layers of its group) groups, dealt
+// to its 16 wavefronts, so a wavefront runs c = ceil(items / 16) <= 3
+// interleaved chains; workgroup times per chain count are measured on gfx950
+// (3 chains = 1000). A block ending with a short record runs all chains for
+// that length, then one chain fewer.
+static void plan_decode(const Shape& s, const cg_level& lv, int32_t n_refs, DecodeArgs* a) {
+  static const int kWgCost[kChains + 1] = {0, 380, 710, 1000};
+  const int lg_max = max_layers_per_group(s, lv);
+  auto chains = [&](int r) { return (r * lg_max + kWaves - 1) / kWaves; };
+  int max_r = 1;
+  while (max_r < kMaxRefsPerBlock && chains(max_r + 1) <= kChains) ++max_r;
+  auto cost = [&](int r, int64_t last) {
+    const int64_t rest = r > 1 ? kWgCost[chains(r - 1)] : 0;
+    return (int64_t)kWgCost[chains(r)] * last / 1024 + rest * (1024 - last) / 1024 + 5;
+  };
+  const BlockPlan p = plan_blocks(n_refs, (int64_t)lv.n_groups * 2 * s.H * s.S, max_r,
+                                  last_len(s, n_refs == n_chunks(s.T, s.C)), cost);
+  a->refs_per_block = p.r1;
+  a->split = p.split;
+  a->refs_per_block2 = p.r2;
+}
+
+// Encode: a workgroup holds R chunks x (layers of its group) groups, dealt
+// round-robin to its 16 wavefronts, which encode theirs one after another;
+// its time is the longest wavefront's sum of chunk lengths.
+static void plan_encode(const Shape& s, const cg_level& lv, int64_t chunk_end, int64_t n, EncodeArgs* a) {
+  const int lg_max = max_layers_per_group(s, lv);
+  auto cost = [&](int r, int64_t last) {
+    int64_t worst = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      int64_t sum = 0;
+      for (int it = w; it < r * lg_max; it += kWaves) sum += it / lg_max == r - 1 ? last : 1024;
+      worst = sum > worst ? sum : worst;
+    }
+    return worst + 5;
+  };
+  const BlockPlan p = plan_blocks(n, (int64_t)lv.n_groups * 2 * s.H * s.S, 4,
+                                  last_len(s, chunk_end == n_chunks(s.T, s.C)), cost);
+  a->chunks_per_block = p.r1;
+  a->split = p.split;
+  a->chunks_per_block2 = p.r2;
+}
+
 extern "C" {
 
 int32_t cg_version(void) { return 1; }
@@ -249,6 +376,7 @@ cg_status cg_encode(const cg_shape* shape, const cg_level* level, const void* ta
   ea.chunk_begin = chunk_begin;
   ea.n_chunks = n;
   ea.cap_words = cap;
+  plan_encode(s, *level, chunk_end, n, &ea);
   ea.scratch = reinterpret_cast<uint16_t*>(ws + w.scratch);
   ea.group_words = reinterpret_cast<uint32_t*>(ws + w.gw);
   ea.group_start = reinterpret_cast<uint32_t*>(ws + w.gs);
@@ -298,94 +426,6 @@ cg_status cg_make_refs(const uint8_t* base_dev, const uint64_t* offsets_dev, int
       !aligned(offsets_dev, 8) || !aligned(refs_dev, 8))
     return CG_ERR_INVALID_ARG;
   return hip_status(launch_make_refs(base_dev, offsets_dev, n, table, refs_dev, stream));
-}
-
-static int compute_units() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    return 256;
-  return cus;
-}
-
-// Decode work plan when every record uses one table set. A workgroup holds
-// R records x (layers of its group) groups, dealt to its 16 wavefronts, so a
-// wavefront runs c = ceil(items / 16) <= 3 interleaved chains. One workgroup
-// fits a compute unit (its tables fill the LDS). Records [0, split) go in
-// blocks of R1 and the rest in blocks of R2; the plan with the shortest
-// simulated greedy dispatch (workgroups taken in launch order by the first
-// free compute unit) wins. Records are taken as full chunks, except that a
-// decode of as many records as the sequence has chunks is taken to end with
-// the sequence's last, shorter chunk (the plan only affects speed).
-// Workgroup times per chain count are measured on gfx950 (3 chains = 1000).
-static void plan_decode(const Shape& s, const cg_level& lv, int32_t n_refs, DecodeArgs* a) {
-  static const int kWgCost[kChains + 1] = {0, 380, 710, 1000};
-  static const int kWgFixed = 5;  // table load and set-up
-  int lg_max = 0;
-  for (int g = 0; g < lv.n_groups; ++g) {
-    int n = 0;
-    for (int l = 0; l < s.L; ++l) n += lv.layer_group[l] == g;
-    if (n > lg_max) lg_max = n;
-  }
-  const int64_t sets = (int64_t)lv.n_groups * 2 * s.H * s.S;
-  const int cus = compute_units();
-  auto chains = [&](int r) { return (r * lg_max + kWaves - 1) / kWaves; };
-  auto cost = [&](int r) { return (int64_t)kWgCost[chains(r)] + kWgFixed; };
-  // length of the last record in units of 1/1024 chunk
-  const int64_t nch = n_chunks(s.T, s.C);
-  const int64_t last = n_refs == nch ? chunk_len(s.T, s.C, nch - 1) * 1024 / s.C : 1024;
-  // a block of r records whose last one is `last` long: all chains for that
-  // length, then one chain fewer for the rest
-  auto cost_last = [&](int r) {
-    const int64_t full = r > 1 ? kWgCost[chains(r - 1)] : 0;
-    return (int64_t)kWgCost[chains(r)] * last / 1024 + full * (1024 - last) / 1024 + kWgFixed;
-  };
-  a->refs_per_block = 1;
-  a->split = 0;
-  a->refs_per_block2 = 1;
-  int64_t best = INT64_MAX;
-  std::vector<int64_t> heap;
-  for (int r1 = 1; r1 <= kMaxRefsPerBlock && r1 <= n_refs && chains(r1) <= kChains; ++r1) {
-    for (int r2 = 1; r2 <= r1; ++r2) {
-      for (int split = 0; split <= n_refs; split += r1) {
-        if (split == n_refs && r2 != 1) continue;  // no second class
-        const int64_t n1 = split / r1, n2 = (n_refs - split + r2 - 1) / r2;
-        int64_t span;
-        if ((n1 + n2) * sets > 200000) {
-          // too many workgroups to simulate: whole rounds
-          const int64_t w1 = n1 * sets, w2 = n2 * sets;
-          span = (w1 + w2 + cus - 1) / cus * (w1 ? cost(r1) : cost(r2));
-        } else {
-          heap.assign(cus, 0);
-          std::make_heap(heap.begin(), heap.end(), std::greater<int64_t>());
-          auto run = [&](int64_t jobs, int64_t t) {
-            for (int64_t k = 0; k < jobs; ++k) {
-              std::pop_heap(heap.begin(), heap.end(), std::greater<int64_t>());
-              heap.back() += t;
-              std::push_heap(heap.begin(), heap.end(), std::greater<int64_t>());
-            }
-          };
-          if (n2 == 0) {
-            run((n1 - 1) * sets, cost(r1));
-            run(sets, cost_last(r1));
-          } else {
-            run(n1 * sets, cost(r1));
-            // the last block holds the last record and may hold fewer records
-            const int64_t rem = (n_refs - split) % r2;
-            run((n2 - 1) * sets, cost(r2));
-            run(sets, cost_last(rem ? (int)rem : r2));
-          }
-          span = *std::max_element(heap.begin(), heap.end());
-        }
-        if (span < best) {
-          best = span;
-          a->refs_per_block = r1;
-          a->split = split;
-          a->refs_per_block2 = r2;
-        }
-      }
-    }
-  }
 }
 
 static cg_status decode_common(const cg_shape* shape, int32_t n_levels, const cg_level* levels,

@@ -537,6 +537,22 @@ __global__ void __launch_bounds__(kNormThreads) k_norm(NormArgs a) {
 constexpr int kEncThreads = kWaves * 64;
 constexpr int kEncBatch = 16;
 
+// On the lanes of m: store the low 16 bits of x at byte voff + soff of sr,
+// then x >>= 16. One masked region with a single VALU shift; the compiler's
+// version computes the shift into a temporary and copies it back.
+__device__ __forceinline__ void renorm_out(uint32_t& x, uint64_t m, __amdgpu_buffer_rsrc_t sr,
+                                           uint32_t voff, uint32_t soff) {
+  uint64_t saved;
+  asm volatile(
+      "s_and_saveexec_b64 %1, %2\n\t"
+      "buffer_store_short %0, %3, %4, %5 offen\n\t"
+      "v_lshrrev_b32 %0, 16, %0\n\t"
+      "s_mov_b64 exec, %1"
+      : "+v"(x), "=&s"(saved)
+      : "s"(m), "v"(voff), "s"(sr), "s"(soff)
+      : "scc", "memory");
+}
+
 // One token t >= 1 of a group, backward: symbol of q_t - q_{t-1}, escape
 // payload, renormalisation word, state update.
 template <bool FAST>
@@ -549,8 +565,8 @@ __device__ __forceinline__ void encode_token(uint16_t xprev, int32_t& qhi, uint3
   const uint32_t d16 = (uint32_t)(qhi - qlo);  // low 16 bits: the wrapped delta
   const uint32_t sraw = sym_raw(qhi, qlo);
   const uint32_t sym = sraw < 255u ? sraw : 255u;
-  const uint32_t e = ftab[sym * 64 + lane];
-  const uint32_t f = e & 0xFFFFu, bb = e >> 16;
+  const uint32_t e = ftab[sym * 64 + lane];  // f | b << 16
+  const uint32_t f = e & 0xFFFFu;
   fmin = f < fmin ? f : fmin;
   const bool is_esc = sraw >= 255u;
   const uint64_t me = __ballot(is_esc);
@@ -562,16 +578,13 @@ __device__ __forceinline__ void encode_token(uint16_t xprev, int32_t& qhi, uint3
   const bool need = (x >> 20) >= f;
   const uint64_t mr = __ballot(need);
   P -= (uint32_t)__popcll(mr);
-  if (need) {
-    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)x, sr, 2u * mbcnt_base(mr, 0), 2u * P, 0);
-    x >>= 16;
-  }
+  renorm_out(x, mr, sr, 2u * mbcnt_base(mr, 0), 2u * P);
   // x <- floor(x/f)*4096 + x mod f + b = x + floor(x/f)*(4096-f) + b; the
   // quotient is < 2^20 and 4096 - f < 2^12, so a 24-bit multiply is exact.
   // (f = 0 only for a symbol missing from the table: the group is then
   // invalid and CG_ERR_TABLE is reported; rcp_tab[0] = 0 keeps it finite)
   const uint32_t qd = (uint32_t)((double)x * rcp_tab[f]);
-  x = x + __umul24(qd, kM - f) + bb;
+  x = __umul24(qd, kM - f) + x + (e >> 16);
   qhi = qlo;
 }
 
@@ -624,9 +637,42 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
   table_err |= (fmin == 0);
 }
 
+// The k-th layer (0-based, ascending) of layer group g, or -1; computed by
+// one wavefront with ballots over the blob's layer -> group map.
+__device__ __forceinline__ int layer_of_group(const uint8_t* blob, int G, int L, int g, int k, int lane) {
+  int base = 0;
+  for (int l0 = 0; l0 < L; l0 += 64) {
+    const int l = l0 + lane;
+    const bool in = l < L && blob_lg(blob, G)[l < L ? l : 0] == g;
+    const uint64_t m = __ballot(in);
+    const int cnt = __popcll(m);
+    if (k < base + cnt) {
+      const uint64_t hit = __ballot(in && (int)mbcnt_base(m, 0) == k - base);
+      return l0 + __builtin_ctzll(hit);
+    }
+    base += cnt;
+  }
+  return -1;
+}
+
+__device__ __forceinline__ int layers_in_group(const uint8_t* blob, int G, int L, int g, int lane) {
+  int n = 0;
+  for (int l0 = 0; l0 < L; l0 += 64) {
+    const int l = l0 + lane;
+    n += __popcll(__ballot(l < L && blob_lg(blob, G)[l < L ? l : 0] == g));
+  }
+  return n;
+}
+
+// LDS of the encoder, laid out by hand so both tables sit at small fixed
+// offsets: the reciprocals first (address f * 8), then the symbol table.
+constexpr int kEncRcpBytes = 8 * (kM + 1);
+constexpr int kEncFtabOff = (kEncRcpBytes + 255) / 256 * 256;
+
 __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
-  __shared__ uint32_t ftab[kEncDwords * 64];
-  __shared__ double rcp_tab[kM + 1];
+  __shared__ __align__(16) uint8_t enc_lds[kEncFtabOff + 4 * kEncDwords * 64];
+  double* rcp_tab = reinterpret_cast<double*>(enc_lds);
+  uint32_t* ftab = reinterpret_cast<uint32_t*>(enc_lds + kEncFtabOff);
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const Shape s = a.s;
   int64_t bid = blockIdx.x;
@@ -637,8 +683,16 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
   const int kv = (int)(bid % 2);
   bid /= 2;
   const int g = (int)(bid % a.G);
-  const int64_t cl = bid / a.G;  // chunk index within the call
-  const int64_t c = a.chunk_begin + cl;
+  const int64_t rb = bid / a.G;  // block of chunks within the call
+  const int64_t nb1 = a.split / a.chunks_per_block;
+  int64_t cl_begin, cl_end;
+  if (rb < nb1) {
+    cl_begin = rb * a.chunks_per_block;
+    cl_end = cl_begin + a.chunks_per_block;
+  } else {
+    cl_begin = a.split + (rb - nb1) * a.chunks_per_block2;
+    cl_end = cl_begin + a.chunks_per_block2 < a.n_chunks ? cl_begin + a.chunks_per_block2 : a.n_chunks;
+  }
   const int G = a.G;
   if (!blob_ok(a.blob, s.L, s.H, s.D, G)) {
     if (tid == 0) set_status(a.status, CG_ERR_INVALID_ARG);
@@ -659,14 +713,18 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
   const float step = blob_step(a.blob, g);
   const float rcp = 1.0f / step;
   const bool fast = qflag(a.blob, s.L, s.H, s.D, G, g);
-  const int64_t n = chunk_len(s.T, s.C, c), t0 = c * s.C;
   const int64_t gpc = groups_per_chunk(s.L, s.H, s.D);
   const uint32_t cap = (uint32_t)a.cap_words;
   bool table_err = false;
-  int cnt = 0;
-  for (int l = 0; l < s.L; ++l) {
-    if (layer_group(a.blob, G, l) != g) continue;
-    if ((cnt++ % kWaves) != wave) continue;
+  // items = (chunk, k-th layer of the group), chunk-major; wavefront w takes
+  // items w, w + 16, ...
+  const int lg_count = layers_in_group(a.blob, G, s.L, g, lane);
+  const int items = (int)(cl_end - cl_begin) * lg_count;
+  for (int it = wave; it < items; it += kWaves) {
+    const int64_t cl = cl_begin + it / lg_count;  // chunk index within the call
+    const int64_t c = a.chunk_begin + cl;
+    const int64_t n = chunk_len(s.T, s.C, c), t0 = c * s.C;
+    const int l = layer_of_group(a.blob, G, s.L, g, it % lg_count, lane);
     const int64_t gi = (((int64_t)l * 2 + kv) * s.H + h) * s.S + j;
     const int64_t slot = cl * gpc + gi;
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.scratch + (size_t)slot * a.cap_words, 2u * cap);
@@ -1293,33 +1351,6 @@ __device__ __forceinline__ void chain_pipe(const DecodeArgs& a, Chain* c, int i0
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// The k-th layer (0-based, ascending) of layer group g, or -1; computed by
-// one wavefront with ballots over the blob's layer -> group map.
-__device__ __forceinline__ int layer_of_group(const uint8_t* blob, int G, int L, int g, int k, int lane) {
-  int base = 0;
-  for (int l0 = 0; l0 < L; l0 += 64) {
-    const int l = l0 + lane;
-    const bool in = l < L && blob_lg(blob, G)[l < L ? l : 0] == g;
-    const uint64_t m = __ballot(in);
-    const int cnt = __popcll(m);
-    if (k < base + cnt) {
-      const uint64_t hit = __ballot(in && (int)mbcnt_base(m, 0) == k - base);
-      return l0 + __builtin_ctzll(hit);
-    }
-    base += cnt;
-  }
-  return -1;
-}
-
-__device__ __forceinline__ int layers_in_group(const uint8_t* blob, int G, int L, int g, int lane) {
-  int n = 0;
-  for (int l0 = 0; l0 < L; l0 += 64) {
-    const int l = l0 + lane;
-    n += __popcll(__ballot(l < L && blob_lg(blob, G)[l < L ? l : 0] == g));
-  }
-  return n;
-}
-
 // NC chains decoded together for their common length, then the longer ones
 // finish one at a time.
 template <bool PAGED, int NC>
@@ -1540,7 +1571,9 @@ hipError_t launch_norm(const NormArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_encode(const EncodeArgs& a, hipStream_t st) {
-  const uint64_t blocks = (uint64_t)a.n_chunks * a.G * 2 * a.s.H * a.s.S;
+  const uint64_t rblocks = (uint64_t)(a.split / a.chunks_per_block) +
+                           (uint64_t)(a.n_chunks - a.split + a.chunks_per_block2 - 1) / a.chunks_per_block2;
+  const uint64_t blocks = rblocks * a.G * 2 * a.s.H * a.s.S;
   hipLaunchKernelGGL(k_encode, dim3((unsigned)blocks), dim3(kEncThreads), 0, st, a);
   return hipGetLastError();
 }

@@ -139,6 +139,9 @@ struct EncodeArgs {
   const uint8_t* blob;
   int G;
   int64_t chunk_begin, n_chunks;
+  // chunks [0, split) of the call go to workgroups in blocks of
+  // chunks_per_block, the rest in blocks of chunks_per_block2
+  int32_t chunks_per_block, split, chunks_per_block2;
   uint64_t cap_words;          // per group slot in the scratch
   uint16_t* scratch;           // [n_chunks][gpc][cap_words]
   uint32_t* group_words;       // [n_chunks][gpc]
