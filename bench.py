@@ -68,7 +68,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
-                    help="per-launch HBM bytes of the dominant kernel from rocprofv3 counters")
+                    help="per-launch HBM bytes of the kernels from rocprofv3 counters")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after the timed steps, one library copy of this many bytes (the calibration "
+                         "launch for the FETCH_SIZE / WRITE_SIZE counter runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; --gpus %d is not supported" % args.gpus,
@@ -79,7 +82,7 @@ def main():
     import torch
 
     from kv_cache_compression_encode_amd import cg as C
-    from kv_cache_compression_encode_amd import codec, synth
+    from kv_cache_compression_encode_amd import codec, profiling, synth
 
     C.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -135,6 +138,12 @@ def main():
     wall = time.perf_counter() - t0
     st = cd.read_status()
     assert st == 0, "codec reported status %d" % st
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        C.cg_copy(dst, src, args.copy_bytes)
+        torch.cuda.synchronize()
+        del src, dst
 
     # per call (all kernels of the call) and per main kernel, mean over the steps
     ms = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in events])
@@ -175,10 +184,12 @@ def main():
         r = {"kernel": name, "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
              "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
              "algorithmic_bytes": int(b), "avg_ms": round(float(t), 4)}
+        # counters taken on these very kernel sources only
         try:
-            tr = json.load(open(args.traffic))
-            ent = tr.get(args.config, {}).get(name)
-            if ent and ent.get("source_hash") == tr.get("kernel_source_hash"):
+            with open(args.traffic) as f:
+                tr = json.load(f).get(args.config, {})
+            ent = tr.get("kernels", {}).get(name)
+            if ent and tr.get("source_hash") == profiling.source_hash():
                 r["traffic"] = ent["bytes_per_launch"]
         except (OSError, ValueError):
             pass

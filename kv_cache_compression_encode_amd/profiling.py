@@ -1,0 +1,143 @@
+"""Summaries of rocprofv3 output for the repository's profiles/ directory.
+
+- ``stats``: per-kernel call counts and durations from a
+  ``rocprofv3 --kernel-trace --stats -f csv`` run, as a markdown table.
+- ``traffic``: HBM bytes per launch of the codec kernels from two
+  ``rocprofv3 --pmc`` runs (FETCH_SIZE, then WRITE_SIZE, both KiB per
+  dispatch), each scaled by what the same counter reads for the library's
+  plain copy kernel (k_copy) moving a known number of bytes. Written as JSON
+  (read by bench.py) and as markdown.
+
+Both record the source hash of the kernels they describe; bench.py reports
+the traffic only while the kernel sources still have that hash.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCES = ("csrc/cg_kernels.hip", "csrc/cg_layout.h", "csrc/cg_api.cpp")
+# kernel symbol fragment -> short name used by bench.py
+KERNELS = {"k_hist": "cg::k_hist(", "k_encode": "cg::k_encode(", "k_decode": "cg::k_decode<false>(",
+           "k_decode_paged": "cg::k_decode<true>(", "k_write": "cg::k_write(", "k_copy": "cg::k_copy("}
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in SOURCES:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _one(pattern: str) -> str:
+    found = sorted(glob.glob(pattern, recursive=True))
+    if not found:
+        raise FileNotFoundError(pattern)
+    return found[0]
+
+
+def kernel_stats(run_dir: str):
+    """[(name, calls, average us, total ms, percent)] from *_kernel_stats.csv."""
+    rows = []
+    with open(_one(os.path.join(run_dir, "**", "*kernel_stats.csv"))) as f:
+        for r in csv.DictReader(f):
+            rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["TotalDurationNs"]) / 1e6, float(r["Percentage"])))
+    rows.sort(key=lambda r: -r[3])
+    return rows
+
+
+def counter_per_kernel(run_dir: str, counter: str):
+    """short kernel name -> mean counter value per dispatch (KiB for the
+    size counters), from *_counter_collection.csv."""
+    vals = {}
+    with open(_one(os.path.join(run_dir, "**", "*counter_collection.csv"))) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            for short, frag in KERNELS.items():
+                if frag in r["Kernel_Name"]:
+                    vals.setdefault(short, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def traffic(fetch_dir: str, write_dir: str, copy_bytes: int):
+    fetch = counter_per_kernel(fetch_dir, "FETCH_SIZE")
+    write = counter_per_kernel(write_dir, "WRITE_SIZE")
+    if "k_copy" not in fetch or "k_copy" not in write:
+        raise ValueError("the runs hold no k_copy dispatch to calibrate against")
+    f_fetch = copy_bytes / (fetch["k_copy"] * 1024.0)
+    f_write = copy_bytes / (write["k_copy"] * 1024.0)
+    out = {"copy_bytes": copy_bytes, "fetch_factor": round(f_fetch, 5), "write_factor": round(f_write, 5),
+           "kernels": {}}
+    for k in sorted(set(fetch) & set(write)):
+        rb = fetch[k] * 1024.0 * f_fetch
+        wb = write[k] * 1024.0 * f_write
+        out["kernels"][k] = {"fetch_kib": round(fetch[k], 1), "write_kib": round(write[k], 1),
+                             "read_bytes": int(rb), "write_bytes": int(wb), "bytes_per_launch": int(rb + wb)}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("run_dir")
+    s.add_argument("--title", required=True)
+    s.add_argument("--command", required=True, help="the command that produced run_dir")
+    s.add_argument("--note", default="")
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True, help="output dir of the FETCH_SIZE run")
+    t.add_argument("--write", required=True, help="output dir of the WRITE_SIZE run")
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--config", required=True, help="workload name the runs used")
+    t.add_argument("--command", required=True, help="the two commands, ';'-separated")
+    t.add_argument("--json", required=True, help="traffic JSON (merged per workload)")
+    t.add_argument("--md", required=True)
+    a = ap.parse_args()
+    if a.cmd == "stats":
+        rows = kernel_stats(a.run_dir)
+        with open(a.out, "w") as f:
+            f.write("# %s\n\n" % a.title)
+            if a.note:
+                f.write(a.note + "\n\n")
+            f.write("Kernel sources: hash `%s`.\n\nCommand (repository root):\n\n```\n%s\n```\n\n"
+                    % (source_hash(), a.command))
+            f.write("| kernel | calls | average us | total ms | % |\n|---|---|---|---|---|\n")
+            for name, calls, avg, tot, pct in rows:
+                f.write("| `%s` | %d | %.1f | %.2f | %.2f |\n" % (name[:90], calls, avg, tot, pct))
+        print("wrote", a.out)
+    else:
+        tr = traffic(a.fetch, a.write, a.copy_bytes)
+        doc = {}
+        if os.path.exists(a.json):
+            with open(a.json) as f:
+                doc = json.load(f)
+        doc[a.config] = dict(tr, source_hash=source_hash())
+        with open(a.json, "w") as f:
+            json.dump(doc, f, indent=1, sort_keys=True)
+        with open(a.md, "w") as f:
+            f.write("# HBM traffic per launch, %s workload (rocprofv3 FETCH_SIZE / WRITE_SIZE)\n\n" % a.config)
+            f.write("Kernel sources: hash `%s`. Calibration: k_copy reads and writes %d bytes; calibrated "
+                    "bytes = counter KiB x 1024 x factor, with factor %.4f for FETCH_SIZE and %.4f for "
+                    "WRITE_SIZE (the copy's known bytes over its counter reading).\n\n"
+                    % (source_hash(), a.copy_bytes, tr["fetch_factor"], tr["write_factor"]))
+            f.write("Commands (repository root):\n\n```\n%s\n```\n\n" % a.command.replace(";", "\n"))
+            f.write("| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes (calibrated) | written bytes "
+                    "(calibrated) | total per launch |\n|---|---|---|---|---|---|\n")
+            for k, v in tr["kernels"].items():
+                f.write("| %s | %.1f | %.1f | %d | %d | %d |\n" % (k, v["fetch_kib"], v["write_kib"],
+                                                                  v["read_bytes"], v["write_bytes"],
+                                                                  v["bytes_per_launch"]))
+        print("wrote", a.json, a.md)
+
+
+if __name__ == "__main__":
+    main()
