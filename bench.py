@@ -195,6 +195,24 @@ def main():
             pass
         return r
 
+    def roof_alu(name):
+        """VALU lane-operations of the kernel (SQ_INSTS_VALU x 64, counted by
+        rocprofv3 on these kernel sources) over its measured time, against the
+        int32 / non-packed fp32 VALU peak of 256 CUs x 64 lanes x 2.4 GHz."""
+        try:
+            with open(args.traffic) as f:
+                tr = json.load(f).get(args.config, {})
+            ent = tr.get("sq", {}).get(name)
+            if not ent or tr.get("source_hash") != profiling.source_hash():
+                return None
+        except (OSError, ValueError):
+            return None
+        ops = ent["SQ_INSTS_VALU"] * 64
+        rate = ops / (phases[name][0] / 1e3) / 1e12
+        peak = profiling.VALU_PEAK_OPS / 1e12
+        return {"kernel": name, "bound": "alu", "achieved": round(rate, 2), "peak": round(peak, 2),
+                "unit": "Tops/s", "frac": round(rate / peak, 4), "valu_ops_per_launch": int(ops)}
+
     res = {
         "metric": METRIC,
         "value": round(fp16_bytes / (wall / args.steps) / 1e9, 2),
@@ -225,6 +243,8 @@ def main():
         "ratio_incl_tables": round(fp16_bytes / (comp + fmt), 3),
         "roofline": roof(dom),
         "roofline_decode": roof("k_decode"),
+        "roofline_alu": roof_alu(dom),
+        "roofline_alu_decode": roof_alu("k_decode"),
         "kernel_ms": {"k_hist": round(kms["build"], 4), "k_encode": round(kms["encode"], 4),
                       "k_decode": round(kms["decode"], 4)},
     }

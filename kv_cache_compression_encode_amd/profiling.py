@@ -84,6 +84,33 @@ def traffic(fetch_dir: str, write_dir: str, copy_bytes: int):
     return out
 
 
+SQ_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS",
+               "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_ANY")
+# int32 / non-packed fp32 VALU lane operations per second: 256 CUs x 4 SIMDs x
+# 16 lanes x 2.4 GHz (= 157.3 TFLOP/s fp32 / 2 for FMA / 2 for packed issue)
+VALU_PEAK_OPS = 256 * 4 * 16 * 2.4e9
+
+
+def sq(sq_dir: str, trace_dir: str):
+    """Per kernel: mean SQ counters per dispatch and, with the kernel-trace
+    average duration, the achieved VALU lane-operation rate."""
+    per = {c: counter_per_kernel(sq_dir, c) for c in SQ_COUNTERS}
+    dur = {}
+    for name, calls, avg_us, tot, pct in kernel_stats(trace_dir):
+        for short, frag in KERNELS.items():
+            if frag in name:
+                dur[short] = avg_us
+    out = {}
+    for k in per["SQ_INSTS_VALU"]:
+        e = {c: per[c].get(k) for c in SQ_COUNTERS}
+        if k in dur:
+            e["avg_us"] = dur[k]
+            e["valu_lane_ops_per_s"] = e["SQ_INSTS_VALU"] * 64 / (dur[k] * 1e-6)
+            e["valu_frac"] = e["valu_lane_ops_per_s"] / VALU_PEAK_OPS
+        out[k] = e
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -101,7 +128,44 @@ def main():
     t.add_argument("--command", required=True, help="the two commands, ';'-separated")
     t.add_argument("--json", required=True, help="traffic JSON (merged per workload)")
     t.add_argument("--md", required=True)
+    q = sub.add_parser("sq")
+    q.add_argument("--sq", required=True, help="output dir of the SQ counter run")
+    q.add_argument("--trace", required=True, help="output dir of a kernel-trace run of the same sources")
+    q.add_argument("--config", required=True)
+    q.add_argument("--command", required=True, help="the command, ';'-separated lines")
+    q.add_argument("--json", required=True)
+    q.add_argument("--md", required=True)
     a = ap.parse_args()
+    if a.cmd == "sq":
+        res = sq(a.sq, a.trace)
+        doc = {}
+        if os.path.exists(a.json):
+            with open(a.json) as f:
+                doc = json.load(f)
+        ent = doc.setdefault(a.config, {})
+        if ent.get("source_hash") not in (None, source_hash()):
+            ent.clear()
+        ent["source_hash"] = source_hash()
+        ent["sq"] = res
+        with open(a.json, "w") as f:
+            json.dump(doc, f, indent=1, sort_keys=True)
+        with open(a.md, "w") as f:
+            f.write("# SQ counters per launch, %s workload (rocprofv3)\n\n" % a.config)
+            f.write("Kernel sources: hash `%s`. VALU peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = %.2f T "
+                    "lane-ops/s (int32 / non-packed fp32). Durations: the kernel-trace run.\n\n"
+                    % (source_hash(), VALU_PEAK_OPS / 1e12))
+            f.write("Commands (repository root):\n\n```\n%s\n```\n\n" % a.command.replace(";", "\n"))
+            f.write("| kernel | avg us | waves | VALU insts | SALU insts | LDS insts | VALU lane-ops/s | of VALU "
+                    "peak | LDS bank conflicts | wait-any / wave-busy |\n|---|---|---|---|---|---|---|---|---|---|\n")
+            for k, e in sorted(res.items()):
+                if "avg_us" not in e:
+                    continue
+                f.write("| %s | %.1f | %d | %.4g | %.4g | %.4g | %.2f T | %.1f %% | %d | %.4g |\n" % (
+                    k, e["avg_us"], e["SQ_WAVES"], e["SQ_INSTS_VALU"], e["SQ_INSTS_SALU"], e["SQ_INSTS_LDS"],
+                    e["valu_lane_ops_per_s"] / 1e12, 100 * e["valu_frac"], e["SQ_LDS_BANK_CONFLICT"] or 0,
+                    e["SQ_WAIT_ANY"] or 0))
+        print("wrote", a.json, a.md)
+        return
     if a.cmd == "stats":
         rows = kernel_stats(a.run_dir)
         with open(a.out, "w") as f:
@@ -120,7 +184,9 @@ def main():
         if os.path.exists(a.json):
             with open(a.json) as f:
                 doc = json.load(f)
-        doc[a.config] = dict(tr, source_hash=source_hash())
+        prev = doc.get(a.config, {})
+        keep = {"sq": prev["sq"]} if prev.get("source_hash") == source_hash() and "sq" in prev else {}
+        doc[a.config] = dict(tr, source_hash=source_hash(), **keep)
         with open(a.json, "w") as f:
             json.dump(doc, f, indent=1, sort_keys=True)
         with open(a.md, "w") as f:
