@@ -120,20 +120,22 @@ __device__ __forceinline__ int32_t quantize(uint16_t xh, float step, float rcp, 
   return is_nan ? 0 : (int32_t)c;
 }
 
-// x_hat = fp16_RNE(fl32(q * step)): two roundings. The empty asm keeps the
-// binary32 product as a value; without it the backend may fuse multiply and
+// x_hat = fp16_RNE(fl32(q * step)): two roundings. The conversion is issued
+// as its own instruction: the backend would fuse the multiply and the
 // conversion into v_fma_mixlo_f16, which rounds once and differs on ties.
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
+  uint32_t h;
+  asm("v_cvt_f16_f32 %0, %1" : "=v"(h) : "v"(v));
+  return (uint16_t)h;
+}
+
 __device__ __forceinline__ uint16_t dequantize(int32_t q, float step) {
-  float v = (float)q * step;
-  asm volatile("" : "+v"(v));
-  return f2h(v);
+  return f32_to_f16_bits((float)q * step);
 }
 
 // Same, for q held modulo 2^16 in the low half of a 32-bit register.
 __device__ __forceinline__ uint16_t dequantize_low16(uint32_t q, float step) {
-  float v = cvt_f32_sext16((int32_t)q) * step;
-  asm volatile("" : "+v"(v));
-  return f2h(v);
+  return f32_to_f16_bits(cvt_f32_sext16((int32_t)q) * step);
 }
 
 // 127 + wrap16(q_t - q_{t-1}) as unsigned: below 255 it is the symbol,
@@ -544,6 +546,7 @@ __device__ __forceinline__ void renorm_out(uint32_t& x, uint64_t m, __amdgpu_buf
                                            uint32_t voff, uint32_t soff) {
   uint64_t saved;
   asm volatile(
+      "s_nop 4\n\t"  // VALU-written SGPR operands of the store: see stream_load_async
       "s_and_saveexec_b64 %1, %2\n\t"
       "buffer_store_short %0, %3, %4, %5 offen\n\t"
       "v_lshrrev_b32 %0, 16, %0\n\t"
@@ -989,6 +992,9 @@ struct Chain {
   uint32_t above, rankx, info, w;
   uint64_t mr;
   int pref_it;  // pipelined loop: iteration that issued the load now in pref
+  // pipelined loop: p and loaded - 128 as byte offsets (2 x words), so the
+  // ring address is one mask and add and the refill test one compare
+  uint32_t pb, lim_b;
 };
 
 struct GroupRef {
@@ -1182,6 +1188,11 @@ __device__ __forceinline__ void chain_steps(const DecodeArgs& a, Chain* c, int i
   }
 }
 
+// v += 2 * k for wave-uniform values, one scalar instruction
+__device__ __forceinline__ void add_twice(uint32_t& v, uint32_t k) {
+  asm("s_lshl1_add_u32 %0, %1, %0" : "+s"(v) : "s"(k) : "scc");
+}
+
 // ---- software-pipelined chains ---------------------------------------------
 // A token of one chain is three phases, each ending in one LDS read that the
 // next phase consumes:
@@ -1220,7 +1231,11 @@ __device__ __forceinline__ void wait_stream_load(int age) {
 // such loads before it returns.
 __device__ __forceinline__ uint32_t stream_load_async(const Chain& c, uint32_t wbase, int lane) {
   uint32_t v;
-  asm volatile("buffer_load_dword %0, %1, %2, 0 offen"
+  // s_nop 4: the compiler does not see the SGPR operands of a memory
+  // instruction inside inline assembly, so it does not insert the 5 wait
+  // states a VALU write of those SGPRs (e.g. a spill reload by v_readlane)
+  // needs before they are read
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, %2, 0 offen"
                : "=&v"(v)
                : "v"(4u * lane + 2u * wbase), "s"(c.src)
                : "memory");
@@ -1229,10 +1244,11 @@ __device__ __forceinline__ uint32_t stream_load_async(const Chain& c, uint32_t w
 
 template <int NC>
 __device__ __forceinline__ void ph_a(Chain& c, const uint32_t* tabs, int lane, int it) {
-  if (c.p > c.loaded - (uint32_t)kRingBlock) {  // fewer than 128 words staged (loaded >= 256)
+  if (c.pb > c.lim_b) {  // fewer than 128 words staged
     wait_stream_load<NC>(it - c.pref_it);
     ring_put(c, c.loaded, c.pref, lane);
     c.loaded += kRingBlock;
+    c.lim_b += 2u * kRingBlock;
     c.pref = stream_load_async(c, c.loaded, lane);
     c.pref_it = it;
     __builtin_amdgcn_wave_barrier();
@@ -1252,7 +1268,8 @@ __device__ __forceinline__ void ph_c(Chain& c) {
   const uint32_t fp = (c.info >> 8) & 0xFFFu, bs = c.info >> 20;
   c.x = x - (fp * (x >> 12) + bs);
   c.mr = __ballot(c.x < kL);
-  const uint16_t* rp = c.ring + (c.p & (kRingWords - 1));
+  const uint16_t* rp =
+      reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(c.ring) + (c.pb & (2u * kRingWords - 1)));
   c.w = rp[mbcnt_base(c.mr, 0)];  // every lane reads; only renormalising lanes use it
 }
 
@@ -1260,13 +1277,14 @@ template <bool PAGED>
 __device__ __forceinline__ void ph_d(const DecodeArgs& a, Chain& c, int i, int h, float step,
                                      uint32_t row_bytes, int lane) {
   renorm_lanes(c.x, c.w, c.mr);
-  c.p += (uint32_t)__popcll(c.mr);
+  add_twice(c.pb, (uint32_t)__popcll(c.mr));
   c.q += (uint32_t)(int32_t)(int8_t)(c.info & 0xFFu);
   const uint64_t me = __ballot((c.info & 0xFFu) == 0x80u);
   if (me) {
-    const uint16_t* ep = c.ring + (c.p & (kRingWords - 1));
+    const uint16_t* ep = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(c.ring) +
+                                                            (c.pb & (2u * kRingWords - 1)));
     if ((c.info & 0xFFu) == 0x80u) c.q += 128u + ep[mbcnt_base(me, 0)];
-    c.p += (uint32_t)__popcll(me);
+    add_twice(c.pb, (uint32_t)__popcll(me));
   }
   const uint16_t y = dequantize_low16(c.q, step);
   if (PAGED)
@@ -1290,7 +1308,11 @@ __device__ __forceinline__ void chain_pipe(const DecodeArgs& a, Chain* c, int i0
   // compiler-issued prefetch of chain_open is complete after this wait
   __builtin_amdgcn_s_waitcnt(0x0F70);
 #pragma unroll
-  for (int k = 0; k < NC; ++k) c[k].pref_it = -8;
+  for (int k = 0; k < NC; ++k) {
+    c[k].pref_it = -8;
+    c[k].pb = 2u * c[k].p;
+    c[k].lim_b = 2u * (c[k].loaded - kRingBlock);
+  }
   // prologue (iteration 0): chain 0 runs A, B, C of token i0; chain 1 A, B;
   // chain 2 A
   ph_a<NC>(c[0], tabs, lane, 0);
@@ -1349,6 +1371,8 @@ __device__ __forceinline__ void chain_pipe(const DecodeArgs& a, Chain* c, int i0
   // the last prefetches may still be in flight into registers the compiler
   // considers free from here on
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int k = 0; k < NC; ++k) c[k].p = c[k].pb >> 1;
 }
 
 // NC chains decoded together for their common length, then the longer ones
