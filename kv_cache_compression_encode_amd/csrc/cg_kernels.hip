@@ -335,26 +335,29 @@ __device__ __forceinline__ void hist_range(__amdgpu_buffer_rsrc_t xr, uint32_t r
     prev = q;
     pos = (pos + 1 == C) ? 0 : pos + 1;
   };
-  int t = t_begin;
-  for (; t + kHistBatch <= t_end; t += kHistBatch) {
-    uint16_t xv[kHistBatch];
-#pragma unroll
-    for (int k = 0; k < kHistBatch; ++k)
-      xv[k] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, (uint32_t)(t + k) * row_bytes, 0);
-#pragma unroll
-    for (int k = 0; k < kHistBatch; ++k) one(xv[k]);
-  }
-  if (t < t_end) {
-    uint16_t xv[kHistBatch];
+  // the rows of the next batch are loaded while the current one is counted
+  // (rows past t_end clamp to the last one)
+  auto load_batch = [&](uint16_t* v, int t0) {
 #pragma unroll
     for (int k = 0; k < kHistBatch; ++k) {
-      const int tk = t + k < t_end ? t + k : t_end - 1;
-      xv[k] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, uni((uint32_t)tk * row_bytes), 0);
+      const int tk = t0 + k < t_end ? t0 + k : t_end - 1;
+      v[k] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, uni((uint32_t)tk * row_bytes), 0);
     }
+  };
+  int t = t_begin;
+  uint16_t xv[kHistBatch];
+  load_batch(xv, t);
+  for (; t + kHistBatch <= t_end; t += kHistBatch) {
+    uint16_t xn[kHistBatch];
+    load_batch(xn, t + kHistBatch);
 #pragma unroll
-    for (int k = 0; k < kHistBatch; ++k)
-      if (t + k < t_end) one(xv[k]);
+    for (int k = 0; k < kHistBatch; ++k) one(xv[k]);
+#pragma unroll
+    for (int k = 0; k < kHistBatch; ++k) xv[k] = xn[k];
   }
+#pragma unroll
+  for (int k = 0; k < kHistBatch; ++k)
+    if (t + k < t_end) one(xv[k]);
 }
 
 __global__ void __launch_bounds__(kHistThreads) k_hist(HistArgs a) {
@@ -541,7 +544,9 @@ constexpr int kEncBatch = 16;
 
 // On the lanes of m: store the low 16 bits of x at byte voff + soff of sr,
 // then x >>= 16. One masked region with a single VALU shift; the compiler's
-// version computes the shift into a temporary and copies it back.
+// version computes the shift into a temporary and copies it back. No memory
+// clobber: nothing in the kernel reads the scratch it writes, and a clobber
+// would keep the next token's table read from moving above the store.
 __device__ __forceinline__ void renorm_out(uint32_t& x, uint64_t m, __amdgpu_buffer_rsrc_t sr,
                                            uint32_t voff, uint32_t soff) {
   uint64_t saved;
@@ -553,7 +558,7 @@ __device__ __forceinline__ void renorm_out(uint32_t& x, uint64_t m, __amdgpu_buf
       "s_mov_b64 exec, %1"
       : "+v"(x), "=&s"(saved)
       : "s"(m), "v"(voff), "s"(sr), "s"(soff)
-      : "scc", "memory");
+      : "scc");
 }
 
 // One token t >= 1 of a group, backward: symbol of q_t - q_{t-1}, escape
@@ -608,27 +613,30 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
   int32_t qhi = quantize<FAST>(
       (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, (uint32_t)(n - 1) * row_bytes, 0), step,
       rcp, d0, d1);
-  int i = n - 1;  // next token to encode
-  for (; i >= kEncBatch; i -= kEncBatch) {
-    uint16_t xv[kEncBatch];
+  // tokens i, i-1, ... take x of rows i-1, i-2, ...; the rows of the next
+  // batch are loaded while the current one is encoded (rows below 0 clamp)
+  auto load_batch = [&](uint16_t* v, int i0) {
 #pragma unroll
-    for (int k = 0; k < kEncBatch; ++k)
-      xv[k] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, (uint32_t)(i - 1 - k) * row_bytes, 0);
+    for (int k = 0; k < kEncBatch; ++k) {
+      const int row = i0 - 1 - k > 0 ? i0 - 1 - k : 0;
+      v[k] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, uni((uint32_t)row * row_bytes), 0);
+    }
+  };
+  int i = n - 1;  // next token to encode
+  uint16_t xv[kEncBatch];
+  load_batch(xv, i);
+  for (; i >= kEncBatch; i -= kEncBatch) {
+    uint16_t xn[kEncBatch];
+    load_batch(xn, i - kEncBatch);
 #pragma unroll
     for (int k = 0; k < kEncBatch; ++k)
       encode_token<FAST>(xv[k], qhi, x, P, step, rcp, ftab, rcp_tab, sr, fmin, lane);
-  }
-  if (i >= 1) {  // the last i < 16 tokens
-    uint16_t xv[kEncBatch];
 #pragma unroll
-    for (int k = 0; k < kEncBatch; ++k) {
-      const int row = i - 1 - k >= 0 ? i - 1 - k : 0;
-      xv[k] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, uni((uint32_t)row * row_bytes), 0);
-    }
-#pragma unroll
-    for (int k = 0; k < kEncBatch; ++k)
-      if (k < i) encode_token<FAST>(xv[k], qhi, x, P, step, rcp, ftab, rcp_tab, sr, fmin, lane);
+    for (int k = 0; k < kEncBatch; ++k) xv[k] = xn[k];
   }
+#pragma unroll
+  for (int k = 0; k < kEncBatch; ++k)  // the last i < 16 tokens
+    if (k < i) encode_token<FAST>(xv[k], qhi, x, P, step, rcp, ftab, rcp_tab, sr, fmin, lane);
   P -= 64;
   __builtin_amdgcn_raw_buffer_store_b16((uint16_t)qhi, sr, lane2, 2u * P, 0);
   P -= 64;
