@@ -207,6 +207,26 @@ cg_status cg_stream_decode_paged(const cg_shape* shape, int32_t n_levels, const 
                                  const int32_t* block_table_dev, int32_t* status_dev,
                                  hipStream_t stream, hipStream_t copy_stream);
 
+/* ---- level policies (host only, no device work) ---------------------------- */
+
+/* Level for one chunk from the bandwidth measured for its transfer, in Gbit/s
+ * ("CacheGen实战" 2.2: the sender watches the link and switches compression
+ * level). Returns 0 (high quality) above 5 Gbit/s, 1 (balanced) above
+ * 1 Gbit/s up to 5, else 2 (fast). The page's comparison operators are
+ * garbled; this is the reading. A NaN bandwidth gives 2. The page's fall back
+ * to sending text and recomputing the cache is not part of the codec. */
+int32_t cg_select_level(double bandwidth_gbps);
+
+/* Recency-based level schedule (the CacheGen technical analysis, dynamic bit
+ * allocation: cache close to the generation position keeps more precision).
+ * Chunk c of n_chunks lies n_chunks - 1 - c chunks behind the newest one; it
+ * gets level 0 (high) when that distance is below near_chunks, level 2
+ * (fast) when it is at least far_chunks, else level 1 (balanced). Writes
+ * levels_host[n_chunks]. Returns CG_ERR_INVALID_ARG unless
+ * 0 <= near_chunks <= far_chunks and n_chunks >= 1. */
+cg_status cg_recency_levels(int64_t n_chunks, int64_t near_chunks, int64_t far_chunks,
+                            int32_t* levels_host);
+
 /* ---- measurement helper ---------------------------------------------------- */
 
 /* Plain device copy of `bytes` (a multiple of 16) with the library's launch

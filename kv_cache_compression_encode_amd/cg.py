@@ -136,6 +136,8 @@ def lib():
         "cg_decode": (i32, [sp, i32, lp, P, P, i32, P, P, pp, P]),
         "cg_decode_paged": (i32, [sp, i32, lp, P, P, i32, P, i64, P, P, pp, P]),
         "cg_copy": (i32, [P, P, u64, P]),
+        "cg_select_level": (i32, [ctypes.c_double]),
+        "cg_recency_levels": (i32, [i64, i64, i64, P]),
         "cg_stream_decode_paged": (i32, [sp, i32, lp, P, P, P, P, i32, P, u64, P, P, i64, P, P, P, P]),
     }
     for name, (res, args) in sigs.items():
@@ -149,7 +151,8 @@ def lib():
 EXPORTS = ("cg_version", "cg_status_string", "cg_tables_bytes", "cg_tables_format_bytes",
            "cg_build_workspace_bytes", "cg_build_tables", "cg_encode_bound",
            "cg_encode_workspace_bytes", "cg_encode", "cg_make_refs", "cg_decode",
-           "cg_decode_paged", "cg_stream_decode_paged", "cg_copy")
+           "cg_decode_paged", "cg_stream_decode_paged", "cg_copy", "cg_select_level",
+           "cg_recency_levels")
 
 
 def status_string(code: int) -> str:
@@ -271,3 +274,14 @@ def cg_stream_decode_paged(shp, levels, tables, records_host, offsets_host, tabl
 
 def cg_copy(dst, src, nbytes, stream=None):
     _check("cg_copy", lib().cg_copy(_ptr(dst), _ptr(src), int(nbytes), _stream(stream)))
+
+
+def cg_select_level(bandwidth_gbps: float) -> int:
+    return lib().cg_select_level(float(bandwidth_gbps))
+
+
+def cg_recency_levels(n_chunks: int, near_chunks: int, far_chunks: int) -> np.ndarray:
+    out = np.zeros(max(int(n_chunks), 1), dtype=np.int32)
+    _check("cg_recency_levels", lib().cg_recency_levels(int(n_chunks), int(near_chunks), int(far_chunks),
+                                                        out.ctypes.data))
+    return out[:int(n_chunks)]

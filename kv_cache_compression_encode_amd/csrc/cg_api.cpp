@@ -578,6 +578,23 @@ cg_status cg_stream_decode_paged(const cg_shape* shape, int32_t n_levels, const 
   return hip_status(e);
 }
 
+int32_t cg_select_level(double bandwidth_gbps) {
+  if (bandwidth_gbps > 5.0) return 0;
+  if (bandwidth_gbps > 1.0) return 1;
+  return 2;  // also NaN
+}
+
+cg_status cg_recency_levels(int64_t n_chunks, int64_t near_chunks, int64_t far_chunks,
+                            int32_t* levels_host) {
+  if (!levels_host || n_chunks < 1 || near_chunks < 0 || far_chunks < near_chunks)
+    return CG_ERR_INVALID_ARG;
+  for (int64_t c = 0; c < n_chunks; ++c) {
+    const int64_t dist = n_chunks - 1 - c;
+    levels_host[c] = dist < near_chunks ? 0 : (dist >= far_chunks ? 2 : 1);
+  }
+  return CG_OK;
+}
+
 cg_status cg_copy(void* dst_dev, const void* src_dev, uint64_t bytes, hipStream_t stream) {
   if (!dst_dev || !src_dev || bytes % 16 != 0 || !aligned(dst_dev, 16) || !aligned(src_dev, 16))
     return CG_ERR_INVALID_ARG;

@@ -193,3 +193,14 @@ def random_kv(L, H, D, T, seed, scale=3.0, rho=0.9, dtype=np.float16):
     z = lfilter([c], [1.0, -rho], e, axis=3)
     s = np.exp(0.5 * rng.standard_normal((L, 2, H, 1, D))) * scale
     return np.clip(z * s, -FP16_MAX, FP16_MAX).astype(dtype)
+
+
+def bandwidth_trace(n: int, seed: int = 0) -> np.ndarray:
+    """Seeded synthetic link bandwidth in Gbit/s, one value per chunk: a
+    random walk in log space between 0.05 and 20 Gbit/s (the pages' links range
+    from 100 Mbit/s to 10 Gbit/s), so every level of the bandwidth policy is
+    visited."""
+    rng = np.random.default_rng([0, 77, seed])
+    steps = rng.normal(0.0, 0.6, n)
+    logb = np.log(3.0) + np.cumsum(steps)
+    return np.exp(np.clip(logb, np.log(0.05), np.log(20.0)))
