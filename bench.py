@@ -139,19 +139,20 @@ def main():
     st = cd.read_status()
     assert st == 0, "codec reported status %d" % st
     # achievable HBM bandwidth on this machine: the library's copy kernel over
-    # 4 GiB (2 x 4 GiB of traffic), best of 3
-    cbytes = 4 << 30
+    # 4 GiB (2 x 4 GiB of traffic), best of 3 (skipped in counter-calibration
+    # runs, whose only copy launch is the calibration one)
+    cbytes = 0 if args.copy_bytes > 0 else 4 << 30
     csrc = torch.empty(cbytes, dtype=torch.uint8, device=dev)
     cdst = torch.empty_like(csrc)
     copy_ms = []
-    for _ in range(3):
+    for _ in range(3 if cbytes else 0):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         C.cg_copy(cdst, csrc, cbytes)
         e1.record(stream)
         e1.synchronize()
         copy_ms.append(e0.elapsed_time(e1))
-    copy_gbps = 2 * cbytes / (min(copy_ms) / 1e3) / 1e9
+    copy_gbps = 2 * cbytes / (min(copy_ms) / 1e3) / 1e9 if cbytes else None
     del csrc, cdst
     if args.copy_bytes > 0:
         src = torch.empty(args.copy_bytes, dtype=torch.uint8, device=dev)
@@ -262,8 +263,9 @@ def main():
         "roofline_alu_decode": roof_alu("k_decode"),
         "kernel_ms": {"k_hist": round(kms["build"], 4), "k_encode": round(kms["encode"], 4),
                       "k_decode": round(kms["decode"], 4)},
-        "copy_GBps": round(copy_gbps, 1),
-        "decode_frac_of_copy": round(phases["k_decode"][1] / (phases["k_decode"][0] / 1e3) / 1e9 / copy_gbps, 4),
+        "copy_GBps": round(copy_gbps, 1) if copy_gbps else None,
+        "decode_frac_of_copy": round(phases["k_decode"][1] / (phases["k_decode"][0] / 1e3) / 1e9 / copy_gbps, 4)
+        if copy_gbps else None,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, X, args.cpu_seconds)

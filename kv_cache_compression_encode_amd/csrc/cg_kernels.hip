@@ -337,27 +337,39 @@ __device__ __forceinline__ void hist_range(__amdgpu_buffer_rsrc_t xr, uint32_t r
   };
   // the rows of the next batch are loaded while the current one is counted
   // (rows past t_end clamp to the last one)
-  auto load_batch = [&](uint16_t* v, int t0) {
+  // (32-bit slots: two 16-bit values packed in one register would make the
+  // packing wait for both loads at once)
+  auto load_batch = [&](uint32_t* v, int t0) {
+    if (t0 + kHistBatch <= t_end) {
+      const uint32_t o0 = (uint32_t)t0 * row_bytes;
 #pragma unroll
-    for (int k = 0; k < kHistBatch; ++k) {
-      const int tk = t0 + k < t_end ? t0 + k : t_end - 1;
-      v[k] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, uni((uint32_t)tk * row_bytes), 0);
+      for (int k = 0; k < kHistBatch; ++k)
+        v[k] = __builtin_amdgcn_raw_buffer_load_b16(xr, lane2, o0 + (uint32_t)k * row_bytes, 0);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kHistBatch; ++k) {
+        const int tk = t0 + k < t_end ? t0 + k : t_end - 1;
+        v[k] = __builtin_amdgcn_raw_buffer_load_b16(xr, lane2, uni((uint32_t)tk * row_bytes), 0);
+      }
     }
   };
   int t = t_begin;
-  uint16_t xv[kHistBatch];
+  uint32_t xv[kHistBatch];
   load_batch(xv, t);
+  // the first batch lands before the loop: otherwise its pending loads merge
+  // into the loop's wait counts and every token waits on the next batch
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   for (; t + kHistBatch <= t_end; t += kHistBatch) {
-    uint16_t xn[kHistBatch];
+    uint32_t xn[kHistBatch];
     load_batch(xn, t + kHistBatch);
 #pragma unroll
-    for (int k = 0; k < kHistBatch; ++k) one(xv[k]);
+    for (int k = 0; k < kHistBatch; ++k) one((uint16_t)xv[k]);
 #pragma unroll
     for (int k = 0; k < kHistBatch; ++k) xv[k] = xn[k];
   }
 #pragma unroll
   for (int k = 0; k < kHistBatch; ++k)
-    if (t + k < t_end) one(xv[k]);
+    if (t + k < t_end) one((uint16_t)xv[k]);
 }
 
 __global__ void __launch_bounds__(kHistThreads) k_hist(HistArgs a) {
@@ -614,29 +626,39 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
       (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, (uint32_t)(n - 1) * row_bytes, 0), step,
       rcp, d0, d1);
   // tokens i, i-1, ... take x of rows i-1, i-2, ...; the rows of the next
-  // batch are loaded while the current one is encoded (rows below 0 clamp)
-  auto load_batch = [&](uint16_t* v, int i0) {
+  // batch are loaded while the current one is encoded. Offsets stay scalar:
+  // a batch of 16 rows all >= 0 needs no clamp; the last one clamps at 0.
+  // (32-bit slots, as in hist_range)
+  auto load_batch = [&](uint32_t* v, int i0) {
+    if (i0 >= kEncBatch) {
+      const uint32_t o0 = (uint32_t)(i0 - 1) * row_bytes;
 #pragma unroll
-    for (int k = 0; k < kEncBatch; ++k) {
-      const int row = i0 - 1 - k > 0 ? i0 - 1 - k : 0;
-      v[k] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, uni((uint32_t)row * row_bytes), 0);
+      for (int k = 0; k < kEncBatch; ++k)
+        v[k] = __builtin_amdgcn_raw_buffer_load_b16(xr, lane2, o0 - (uint32_t)k * row_bytes, 0);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kEncBatch; ++k) {
+        const int row = i0 - 1 - k > 0 ? i0 - 1 - k : 0;
+        v[k] = __builtin_amdgcn_raw_buffer_load_b16(xr, lane2, uni((uint32_t)row * row_bytes), 0);
+      }
     }
   };
   int i = n - 1;  // next token to encode
-  uint16_t xv[kEncBatch];
+  uint32_t xv[kEncBatch];
   load_batch(xv, i);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // as in hist_range
   for (; i >= kEncBatch; i -= kEncBatch) {
-    uint16_t xn[kEncBatch];
+    uint32_t xn[kEncBatch];
     load_batch(xn, i - kEncBatch);
 #pragma unroll
     for (int k = 0; k < kEncBatch; ++k)
-      encode_token<FAST>(xv[k], qhi, x, P, step, rcp, ftab, rcp_tab, sr, fmin, lane);
+      encode_token<FAST>((uint16_t)xv[k], qhi, x, P, step, rcp, ftab, rcp_tab, sr, fmin, lane);
 #pragma unroll
     for (int k = 0; k < kEncBatch; ++k) xv[k] = xn[k];
   }
 #pragma unroll
   for (int k = 0; k < kEncBatch; ++k)  // the last i < 16 tokens
-    if (k < i) encode_token<FAST>(xv[k], qhi, x, P, step, rcp, ftab, rcp_tab, sr, fmin, lane);
+    if (k < i) encode_token<FAST>((uint16_t)xv[k], qhi, x, P, step, rcp, ftab, rcp_tab, sr, fmin, lane);
   P -= 64;
   __builtin_amdgcn_raw_buffer_store_b16((uint16_t)qhi, sr, lane2, 2u * P, 0);
   P -= 64;
