@@ -573,39 +573,55 @@ __device__ __forceinline__ void renorm_out(uint32_t& x, uint64_t m, __amdgpu_buf
       : "scc");
 }
 
-// One token t >= 1 of a group, backward: symbol of q_t - q_{t-1}, escape
-// payload, renormalisation word, state update.
+// A token t >= 1 of a group passes three stages, each started one token
+// after the previous one so that its LDS read lands behind a token of other
+// work instead of being waited for at once:
+//   S1: quantize x_{t-1}, symbol of q_t - q_{t-1}, read the symbol's entry
+//   S2: f of the entry, read RU(1/f)
+//   S3: escape payload, renormalisation word, state update
+struct EncTok {
+  uint32_t e;    // symbol entry f | b << 16 (S1 read)
+  uint32_t d16;  // low 16 bits: the wrapped delta, the escape payload
+  bool esc;      // this lane's delta needs an escape
+  uint64_t me;   // lanes of the wavefront that need one
+  uint32_t f;
+  double r;      // RU(1/f) (S2 read)
+};
+
 template <bool FAST>
-__device__ __forceinline__ void encode_token(uint16_t xprev, int32_t& qhi, uint32_t& x, uint32_t& P,
-                                             float step, float rcp, const uint32_t* ftab,
-                                             const double* rcp_tab, __amdgpu_buffer_rsrc_t sr,
-                                             uint32_t& fmin, int lane) {
+__device__ __forceinline__ void enc_s1(EncTok& k, uint16_t xprev, int32_t& qhi, float step, float rcp,
+                                       const uint32_t* ftab, int lane) {
   uint32_t d0 = 0, d1 = 0;
   const int32_t qlo = quantize<FAST>(xprev, step, rcp, d0, d1);
-  const uint32_t d16 = (uint32_t)(qhi - qlo);  // low 16 bits: the wrapped delta
+  k.d16 = (uint32_t)(qhi - qlo);
   const uint32_t sraw = sym_raw(qhi, qlo);
-  const uint32_t sym = sraw < 255u ? sraw : 255u;
-  const uint32_t e = ftab[sym * 64 + lane];  // f | b << 16
-  const uint32_t f = e & 0xFFFFu;
-  fmin = f < fmin ? f : fmin;
-  const bool is_esc = sraw >= 255u;
-  const uint64_t me = __ballot(is_esc);
-  if (me) {
-    P -= (uint32_t)__popcll(me);
-    if (is_esc) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)d16, sr, 2u * mbcnt_base(me, 0), 2u * P, 0);
+  k.e = ftab[(sraw < 255u ? sraw : 255u) * 64 + lane];
+  k.esc = sraw >= 255u;
+  k.me = __ballot(k.esc);
+  qhi = qlo;
+}
+
+__device__ __forceinline__ void enc_s2(EncTok& k, const double* rcp_tab, uint32_t& fmin) {
+  k.f = k.e & 0xFFFFu;
+  fmin = k.f < fmin ? k.f : fmin;
+  k.r = rcp_tab[k.f];
+}
+
+__device__ __forceinline__ void enc_s3(const EncTok& k, uint32_t& x, uint32_t& P, __amdgpu_buffer_rsrc_t sr) {
+  if (k.me) {
+    P -= (uint32_t)__popcll(k.me);
+    if (k.esc) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)k.d16, sr, 2u * mbcnt_base(k.me, 0), 2u * P, 0);
   }
   // renormalise when x >= f * 2^20, i.e. floor(x / 2^20) >= f (never for f = 4096)
-  const bool need = (x >> 20) >= f;
-  const uint64_t mr = __ballot(need);
+  const uint64_t mr = __ballot((x >> 20) >= k.f);
   P -= (uint32_t)__popcll(mr);
   renorm_out(x, mr, sr, 2u * mbcnt_base(mr, 0), 2u * P);
   // x <- floor(x/f)*4096 + x mod f + b = x + floor(x/f)*(4096-f) + b; the
   // quotient is < 2^20 and 4096 - f < 2^12, so a 24-bit multiply is exact.
   // (f = 0 only for a symbol missing from the table: the group is then
   // invalid and CG_ERR_TABLE is reported; rcp_tab[0] = 0 keeps it finite)
-  const uint32_t qd = (uint32_t)((double)x * rcp_tab[f]);
-  x = __umul24(qd, kM - f) + x + (e >> 16);
-  qhi = qlo;
+  const uint32_t qd = (uint32_t)((double)x * k.r);
+  x = __umul24(qd, kM - k.f) + x + (k.e >> 16);
 }
 
 // Encodes tokens n-1 .. 1 of a group (backward), then the head. xr covers the
@@ -621,44 +637,66 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
   uint32_t P = cap;
   uint32_t x = kL;
   uint32_t fmin = 0xFFFFFFFFu;
+  auto row = [&](int r) { return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, (uint32_t)r * row_bytes, 0); };
   uint32_t d0 = 0, d1 = 0;
-  int32_t qhi = quantize<FAST>(
-      (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, (uint32_t)(n - 1) * row_bytes, 0), step,
-      rcp, d0, d1);
-  // tokens i, i-1, ... take x of rows i-1, i-2, ...; the rows of the next
-  // batch are loaded while the current one is encoded. Offsets stay scalar:
-  // a batch of 16 rows all >= 0 needs no clamp; the last one clamps at 0.
-  // (32-bit slots, as in hist_range)
-  auto load_batch = [&](uint32_t* v, int i0) {
-    if (i0 >= kEncBatch) {
-      const uint32_t o0 = (uint32_t)(i0 - 1) * row_bytes;
+  int32_t qhi = quantize<FAST>(row(n - 1), step, rcp, d0, d1);
+  if (n >= 3) {
+    // a: token in S3, b: in S2, c: in S1. Prologue: token n-1 through S1 and
+    // S2, token n-2 through S1.
+    EncTok a, b, c;
+    enc_s1<FAST>(a, row(n - 2), qhi, step, rcp, ftab, lane);
+    enc_s2(a, rcp_tab, fmin);
+    enc_s1<FAST>(b, row(n - 3), qhi, step, rcp, ftab, lane);
+    // tokens i, i-1, ... enter S1 with x of rows i-1, i-2, ...; the rows of
+    // the next batch are loaded while the current one is encoded. Offsets
+    // stay scalar: a batch of 16 rows all >= 0 needs no clamp; the last one
+    // clamps at 0. (32-bit slots, as in hist_range)
+    auto load_batch = [&](uint32_t* v, int i0) {
+      if (i0 >= kEncBatch) {
+        const uint32_t o0 = (uint32_t)(i0 - 1) * row_bytes;
 #pragma unroll
-      for (int k = 0; k < kEncBatch; ++k)
-        v[k] = __builtin_amdgcn_raw_buffer_load_b16(xr, lane2, o0 - (uint32_t)k * row_bytes, 0);
-    } else {
+        for (int k = 0; k < kEncBatch; ++k)
+          v[k] = __builtin_amdgcn_raw_buffer_load_b16(xr, lane2, o0 - (uint32_t)k * row_bytes, 0);
+      } else {
 #pragma unroll
-      for (int k = 0; k < kEncBatch; ++k) {
-        const int row = i0 - 1 - k > 0 ? i0 - 1 - k : 0;
-        v[k] = __builtin_amdgcn_raw_buffer_load_b16(xr, lane2, uni((uint32_t)row * row_bytes), 0);
+        for (int k = 0; k < kEncBatch; ++k) {
+          const int r = i0 - 1 - k > 0 ? i0 - 1 - k : 0;
+          v[k] = __builtin_amdgcn_raw_buffer_load_b16(xr, lane2, uni((uint32_t)r * row_bytes), 0);
+        }
       }
+    };
+    int i = n - 3;  // next token to enter S1
+    uint32_t xv[kEncBatch];
+    load_batch(xv, i);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // as in hist_range
+    auto advance = [&](uint16_t xprev) {
+      enc_s1<FAST>(c, xprev, qhi, step, rcp, ftab, lane);
+      enc_s2(b, rcp_tab, fmin);
+      enc_s3(a, x, P, sr);
+      a = b;
+      b = c;
+    };
+    for (; i >= kEncBatch; i -= kEncBatch) {
+      uint32_t xn[kEncBatch];
+      load_batch(xn, i - kEncBatch);
+#pragma unroll
+      for (int k = 0; k < kEncBatch; ++k) advance((uint16_t)xv[k]);
+#pragma unroll
+      for (int k = 0; k < kEncBatch; ++k) xv[k] = xn[k];
     }
-  };
-  int i = n - 1;  // next token to encode
-  uint32_t xv[kEncBatch];
-  load_batch(xv, i);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // as in hist_range
-  for (; i >= kEncBatch; i -= kEncBatch) {
-    uint32_t xn[kEncBatch];
-    load_batch(xn, i - kEncBatch);
 #pragma unroll
-    for (int k = 0; k < kEncBatch; ++k)
-      encode_token<FAST>((uint16_t)xv[k], qhi, x, P, step, rcp, ftab, rcp_tab, sr, fmin, lane);
-#pragma unroll
-    for (int k = 0; k < kEncBatch; ++k) xv[k] = xn[k];
+    for (int k = 0; k < kEncBatch; ++k)  // the last i < 16 tokens
+      if (k < i) advance((uint16_t)xv[k]);
+    // epilogue: the last two tokens leave the pipeline
+    enc_s2(b, rcp_tab, fmin);
+    enc_s3(a, x, P, sr);
+    enc_s3(b, x, P, sr);
+  } else if (n == 2) {
+    EncTok a;
+    enc_s1<FAST>(a, row(0), qhi, step, rcp, ftab, lane);
+    enc_s2(a, rcp_tab, fmin);
+    enc_s3(a, x, P, sr);
   }
-#pragma unroll
-  for (int k = 0; k < kEncBatch; ++k)  // the last i < 16 tokens
-    if (k < i) encode_token<FAST>((uint16_t)xv[k], qhi, x, P, step, rcp, ftab, rcp_tab, sr, fmin, lane);
   P -= 64;
   __builtin_amdgcn_raw_buffer_store_b16((uint16_t)qhi, sr, lane2, 2u * P, 0);
   P -= 64;
