@@ -195,6 +195,25 @@ def random_kv(L, H, D, T, seed, scale=3.0, rho=0.9, dtype=np.float16):
     return np.clip(z * s, -FP16_MAX, FP16_MAX).astype(dtype)
 
 
+BF16_MAX = 3.3895313892515355e38
+
+
+def random_kv_bf16(L, H, D, T, seed, scale=3.0, rho=0.9):
+    """As random_kv, as raw bfloat16 bits (uint16): the same AR(1) draw,
+    rounded to nearest-even bfloat16 by torch. A large `scale` exercises the
+    range bfloat16 has beyond fp16."""
+    import torch
+    from scipy.signal import lfilter
+    rng = np.random.default_rng(seed)
+    e = rng.standard_normal((L, 2, H, T, D))
+    c = np.sqrt(1 - rho * rho)
+    e[:, :, :, 0, :] /= c
+    z = lfilter([c], [1.0, -rho], e, axis=3)
+    s = np.exp(0.5 * rng.standard_normal((L, 2, H, 1, D))) * scale
+    x = np.clip(z * s, -BF16_MAX, BF16_MAX).astype(np.float32)
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
 def bandwidth_trace(n: int, seed: int = 0) -> np.ndarray:
     """Seeded synthetic link bandwidth in Gbit/s, one value per chunk: a
     random walk in log space between 0.05 and 20 Gbit/s (the pages' links range

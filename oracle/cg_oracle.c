@@ -20,7 +20,8 @@
  *  [P1] "CacheGen：大语言模型推理加速的KV缓存压缩与流式传输技术解析"
  *       「KV缓存的量化压缩机制」: K and V are 16-bit FP16/BF16 tensors;
  *       「量化编码器设计」: statistics are taken per channel and the quantized
- *       integer indices are entropy coded;
+ *       integer indices are entropy coded; the coder's statistics may come
+ *       from a calibration run on other data (robust tables, below);
  *       「流式传输架构」: the compressed cache travels as independent chunks.
  *  [P3] KV-cache optimisation article (test.idctop.com),
  *       「vLLM中的PagedAttention优化」: KV held in physical blocks that need
@@ -51,6 +52,10 @@
 #define CGO_ERR_CORRUPT (-5)
 #define CGO_ERR_TABLE (-6)
 
+#define CGO_F16 0                    /* element types of the KV tensor  */
+#define CGO_BF16 1
+#define CGO_TABLES_ROBUST 1u         /* tables flag: unseen symbols escape */
+
 #define CGO_TABLE_MAGIC 0x42544743u  /* "CGTB" */
 #define CGO_RECORD_MAGIC 0x4B434743u /* "CGCK" */
 #define CGO_VERSION 1u
@@ -61,6 +66,8 @@ typedef struct {
   int32_t head_dim;
   int32_t chunk_tokens;
   int64_t tokens;
+  int32_t dtype;     /* CGO_F16 or CGO_BF16: the element type of x and y */
+  int32_t reserved;  /* 0 */
 } cgo_shape;
 
 /* ------------------------------------------------------------------------ */
@@ -130,13 +137,66 @@ uint16_t cgo_float_to_half(float f) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* bfloat16 <-> binary32, from the format: sign, 8-bit exponent (bias 127),  */
+/* 7-bit fraction. [P1]「KV缓存的量化压缩机制」: BF16 is the other 16-bit    */
+/* type the cache may hold.                                                   */
+/* ------------------------------------------------------------------------ */
+float cgo_bf16_to_float(uint16_t h) {
+  uint32_t sign = h >> 15, e = (h >> 7) & 255u, m = h & 127u;
+  float v;
+  if (e == 0) {
+    v = ldexpf((float)m, -133);               /* zero or subnormal: m * 2^-133 */
+  } else if (e == 255) {
+    if (m == 0) {
+      v = INFINITY;
+    } else {                                  /* NaN: keep the payload bits  */
+      uint32_t bits = 0x7F800000u | (m << 16);
+      memcpy(&v, &bits, 4);
+    }
+  } else {
+    v = ldexpf((float)(128u + m), (int)e - 134); /* (1.m) * 2^(e-127)        */
+  }
+  return sign ? -v : v;
+}
+
+/* Round to nearest, ties to even; NaN stays a (quiet) NaN. */
+uint16_t cgo_float_to_bf16(float f) {
+  uint32_t bits;
+  memcpy(&bits, &f, 4);
+  uint16_t sign = (uint16_t)((bits >> 16) & 0x8000u);
+  if (isnan(f)) return (uint16_t)(sign | 0x7FC0u | ((bits >> 16) & 0x7Fu));
+  double a = fabs((double)f);
+  /* halfway between the largest finite value (2 - 2^-7) * 2^127 and 2^128;
+   * the tie goes to the even neighbour, which is the overflow */
+  if (a >= ldexp(2.0 - ldexp(1.0, -8), 127)) return (uint16_t)(sign | 0x7F80u);
+  if (a < ldexp(1.0, -126)) {
+    /* subnormal range: multiples of 2^-133; 128 becomes the smallest normal */
+    double n = rint(a * ldexp(1.0, 133));
+    return (uint16_t)(sign | (uint16_t)n);
+  }
+  int ex;
+  frexp(a, &ex);
+  int E = ex - 1;                    /* a in [2^E, 2^(E+1))                   */
+  double n = rint(ldexp(a, 7 - E));  /* significand scaled to [128, 256]      */
+  if (n >= 256.0) { n = 128.0; E += 1; }
+  return (uint16_t)(sign | (uint16_t)((E + 127) << 7) | (uint16_t)((uint32_t)n - 128u));
+}
+
+static float elem_to_float(int dtype, uint16_t h) {
+  return dtype == CGO_BF16 ? cgo_bf16_to_float(h) : cgo_half_to_float(h);
+}
+static uint16_t float_to_elem(int dtype, float f) {
+  return dtype == CGO_BF16 ? cgo_float_to_bf16(f) : cgo_float_to_half(f);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Quantization. [P2] section 1: one uniform step per layer group, finer in  */
 /* shallow layers; presets in section 3.1.                                    */
 /* READING: q = round-half-even(fl32(x / step)) with an IEEE binary32 divide, */
 /* clamped to int16; NaN gives 0. Saturation is counted.                       */
 /* ------------------------------------------------------------------------ */
-int32_t cgo_quantize(uint16_t xh, float step, int* saturated, int* is_nan) {
-  float x = cgo_half_to_float(xh);
+int32_t cgo_quantize_dt(int dtype, uint16_t xh, float step, int* saturated, int* is_nan) {
+  float x = elem_to_float(dtype, xh);
   if (saturated) *saturated = 0;
   if (is_nan) *is_nan = 0;
   if (isnan(x)) {
@@ -156,11 +216,17 @@ int32_t cgo_quantize(uint16_t xh, float step, int* saturated, int* is_nan) {
   return (int32_t)r;
 }
 
-/* READING: reconstruction = fp16_RNE(fl32(float(q) * step)). */
-uint16_t cgo_dequantize(int32_t q, float step) {
-  float v = (float)q * step;    /* one binary32 product, no contraction      */
-  return cgo_float_to_half(v);
+int32_t cgo_quantize(uint16_t xh, float step, int* saturated, int* is_nan) {
+  return cgo_quantize_dt(CGO_F16, xh, step, saturated, is_nan);
 }
+
+/* READING: reconstruction = RNE to the element type of fl32(float(q) * step). */
+uint16_t cgo_dequantize_dt(int dtype, int32_t q, float step) {
+  float v = (float)q * step;    /* one binary32 product, no contraction      */
+  return float_to_elem(dtype, v);
+}
+
+uint16_t cgo_dequantize(int32_t q, float step) { return cgo_dequantize_dt(CGO_F16, q, step); }
 
 /* Array forms of the scalar definitions above (plain loops, for tests). */
 void cgo_half_to_float_array(const uint16_t* h, int64_t n, float* out) {
@@ -174,6 +240,18 @@ void cgo_quantize_array(const uint16_t* xh, int64_t n, float step, int32_t* q) {
 }
 void cgo_dequantize_array(const int32_t* q, int64_t n, float step, uint16_t* out) {
   for (int64_t i = 0; i < n; i++) out[i] = cgo_dequantize(q[i], step);
+}
+void cgo_bf16_to_float_array(const uint16_t* h, int64_t n, float* out) {
+  for (int64_t i = 0; i < n; i++) out[i] = cgo_bf16_to_float(h[i]);
+}
+void cgo_float_to_bf16_array(const float* f, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; i++) out[i] = cgo_float_to_bf16(f[i]);
+}
+void cgo_quantize_array_dt(int dtype, const uint16_t* xh, int64_t n, float step, int32_t* q) {
+  for (int64_t i = 0; i < n; i++) q[i] = cgo_quantize_dt(dtype, xh[i], step, 0, 0);
+}
+void cgo_dequantize_array_dt(int dtype, const int32_t* q, int64_t n, float step, uint16_t* out) {
+  for (int64_t i = 0; i < n; i++) out[i] = cgo_dequantize_dt(dtype, q[i], step);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -190,8 +268,8 @@ int32_t cgo_wrap16(int32_t v) {
 }
 
 static int symbol_of(int32_t d, uint16_t* payload) {
-  if (d >= -127 && d <= 127) return d + 127;
   *payload = (uint16_t)(d & 0xFFFF);
+  if (d >= -127 && d <= 127) return d + 127;
   return CGO_ESC;
 }
 
@@ -212,7 +290,8 @@ static size_t x_index(const cgo_shape* s, int l, int kv, int h, int64_t t, int d
 
 static int shape_ok(const cgo_shape* s) {
   return s && s->layers > 0 && s->kv_heads > 0 && s->head_dim > 0 && s->head_dim % 64 == 0 &&
-         s->chunk_tokens > 0 && s->tokens > 0;
+         s->chunk_tokens > 0 && s->tokens > 0 && (s->dtype == CGO_F16 || s->dtype == CGO_BF16) &&
+         s->reserved == 0;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -234,7 +313,7 @@ void cgo_table_counts(const cgo_shape* s, const uint8_t* layer_group, const floa
       int32_t prev = 0;
       for (int64_t i = 0; i < n; i++) {
         int sat, nan_;
-        int32_t q = cgo_quantize(X[x_index(s, l, kv, h, t0 + i, d)], step, &sat, &nan_);
+        int32_t q = cgo_quantize_dt(s->dtype, X[x_index(s, l, kv, h, t0 + i, d)], step, &sat, &nan_);
         if (stats) {
           stats[0] += 1;
           stats[1] += (uint64_t)sat;
@@ -289,6 +368,22 @@ void cgo_normalize(const uint64_t counts[256], uint16_t f[256]) {
   }
 }
 
+/* READING: robust tables ([P1]「量化编码器设计」: the statistics may come
+ * from calibration data other than the tensor coded). Normalise as above;
+ * if the escape symbol got no frequency, one unit moves to it from the
+ * largest frequency (lowest symbol on ties), so that every delta stays
+ * codable: a delta whose symbol has f = 0 is coded as an escape. */
+void cgo_normalize_robust(const uint64_t counts[256], uint16_t f[256]) {
+  cgo_normalize(counts, f);
+  if (f[CGO_ESC] == 0) {
+    int j = 0;
+    for (int s = 1; s < 256; s++)
+      if (f[s] > f[j]) j = s;
+    f[j] = (uint16_t)(f[j] - 1u);
+    f[CGO_ESC] = 1;
+  }
+}
+
 /* Cumulative frequencies: b[s] = sum of f over symbols below s. */
 static void cumulative(const uint16_t f[256], uint32_t b[256]) {
   uint32_t acc = 0;
@@ -302,7 +397,7 @@ static void cumulative(const uint16_t f[256], uint32_t b[256]) {
 /* Tables blob (format section). Little-endian:                              */
 /*   0 magic "CGTB"   4 version   8 layers  12 kv_heads  16 head_dim         */
 /*  20 n_groups      24 level_id 28 chunk_tokens  32 tokens (u64)            */
-/*  40 f_offset      44 zero     48 format_bytes (u64)   56 zero (u64)       */
+/*  40 f_offset      44 dtype    48 format_bytes (u64)   56 flags  60 zero    */
 /*  64 f32 step[G], then u8 layer_group[L], zero pad to f_offset             */
 /*     (= align 256), then u16 f[G][2][H][D][256].                           */
 /* ------------------------------------------------------------------------ */
@@ -319,12 +414,14 @@ static size_t table_index(const cgo_shape* s, int g, int kv, int h, int d) {
   return (((size_t)g * 2 + kv) * s->kv_heads + h) * s->head_dim + d;
 }
 
-/* Builds the tables of one quality level from the tensor it will encode.
+/* Builds the tables of one quality level from X (the tensor to encode, or
+ * calibration data for robust tables: flags = CGO_TABLES_ROBUST).
  * stats (optional) = {elements, saturated, nan, escapes}. */
 int cgo_build_tables(const cgo_shape* s, int32_t level_id, int32_t n_groups,
                      const uint8_t* layer_group, const float* steps, const uint16_t* X,
-                     uint8_t* blob, uint64_t blob_cap, uint64_t stats[4]) {
+                     uint32_t flags, uint8_t* blob, uint64_t blob_cap, uint64_t stats[4]) {
   if (!shape_ok(s) || n_groups < 1 || n_groups > 255) return CGO_ERR_INVALID_ARG;
+  if (flags & ~CGO_TABLES_ROBUST) return CGO_ERR_INVALID_ARG;
   for (int l = 0; l < s->layers; l++)
     if (layer_group[l] >= n_groups) return CGO_ERR_INVALID_ARG;
   for (int g = 0; g < n_groups; g++)
@@ -343,7 +440,9 @@ int cgo_build_tables(const cgo_shape* s, int32_t level_id, int32_t n_groups,
   put_u32(blob + 28, (uint32_t)s->chunk_tokens);
   put_u64(blob + 32, (uint64_t)s->tokens);
   put_u32(blob + 40, (uint32_t)foff);
+  put_u32(blob + 44, (uint32_t)s->dtype);
   put_u64(blob + 48, need);
+  put_u32(blob + 56, flags);
   for (int g = 0; g < n_groups; g++) {
     uint32_t bits;
     memcpy(&bits, &steps[g], 4);
@@ -358,7 +457,10 @@ int cgo_build_tables(const cgo_shape* s, int32_t level_id, int32_t n_groups,
       for (int h = 0; h < s->kv_heads; h++)
         for (int d = 0; d < s->head_dim; d++) {
           cgo_table_counts(s, layer_group, steps, X, g, kv, h, d, counts, stats);
-          cgo_normalize(counts, f);
+          if (flags & CGO_TABLES_ROBUST)
+            cgo_normalize_robust(counts, f);
+          else
+            cgo_normalize(counts, f);
           uint8_t* dst = blob + foff + table_index(s, g, kv, h, d) * 512;
           for (int k = 0; k < 256; k++) put_u16(dst + 2 * k, f[k]);
         }
@@ -367,6 +469,7 @@ int cgo_build_tables(const cgo_shape* s, int32_t level_id, int32_t n_groups,
 
 typedef struct {
   int32_t n_groups, level_id;
+  int robust;
   float steps[256];
   uint8_t lg[65536];
   const uint8_t* f;
@@ -379,6 +482,10 @@ static int parse_blob(const cgo_shape* s, const uint8_t* blob, blob_view* v) {
     return CGO_ERR_INVALID_ARG;
   v->n_groups = (int32_t)get_u32(blob + 20);
   v->level_id = (int32_t)get_u32(blob + 24);
+  if ((int32_t)get_u32(blob + 44) != s->dtype) return CGO_ERR_INVALID_ARG;
+  uint32_t flags = get_u32(blob + 56);
+  if (flags & ~CGO_TABLES_ROBUST) return CGO_ERR_INVALID_ARG;
+  v->robust = (flags & CGO_TABLES_ROBUST) != 0;
   if (v->n_groups < 1 || v->n_groups > 255) return CGO_ERR_INVALID_ARG;
   for (int g = 0; g < v->n_groups; g++) {
     uint32_t bits = get_u32(blob + 64 + 4 * g);
@@ -410,6 +517,8 @@ static void load_table(const cgo_shape* s, const blob_view* v, int g, int kv, in
 /* The encoder runs i = n-1 down to 1; for each lane it first renormalises   */
 /* (emits the low 16 bits when x >= f*2^20) and then codes the symbol:       */
 /*   x <- floor(x/f)*4096 + (x mod f) + b.                                    */
+/* With robust tables a symbol of frequency 0 is coded as the escape (its   */
+/* delta becomes the payload); otherwise it is an error (CGO_ERR_TABLE).    */
 /* ------------------------------------------------------------------------ */
 static void group_q(const cgo_shape* s, const blob_view* v, const uint16_t* X, int64_t c, int l,
                     int kv, int h, int j, int32_t* q /* [64][n] */, int64_t n) {
@@ -417,14 +526,14 @@ static void group_q(const cgo_shape* s, const blob_view* v, const uint16_t* X, i
   float step = v->steps[v->lg[l]];
   for (int k = 0; k < CGO_LANES; k++)
     for (int64_t i = 0; i < n; i++)
-      q[k * n + i] = cgo_quantize(X[x_index(s, l, kv, h, t0 + i, 64 * j + k)], step, 0, 0);
+      q[k * n + i] = cgo_quantize_dt(s->dtype, X[x_index(s, l, kv, h, t0 + i, 64 * j + k)], step, 0, 0);
 }
 
 /* Worst case: one renorm word and one escape word per symbol, plus the head. */
 int64_t cgo_group_word_bound(int64_t n) { return CGO_LANES * (2 * (n - 1) + 3); }
 
 int64_t cgo_encode_group_q(const int32_t* q /* [64][n] */, int64_t n,
-                           const uint16_t* const f_lane[64], uint16_t* out, int64_t cap) {
+                           const uint16_t* const f_lane[64], int robust, uint16_t* out, int64_t cap) {
   uint32_t b[64][256];
   for (int k = 0; k < CGO_LANES; k++) cumulative(f_lane[k], b[k]);
   int64_t steps = n > 1 ? n - 1 : 0;
@@ -440,6 +549,7 @@ int64_t cgo_encode_group_q(const int32_t* q /* [64][n] */, int64_t n,
     for (int k = 0; k < CGO_LANES; k++) {
       uint16_t pay = 0;
       int sym = symbol_of(cgo_wrap16(q[k * n + i] - q[k * n + i - 1]), &pay);
+      if (robust && f_lane[k][sym] == 0) sym = CGO_ESC;
       uint32_t f = f_lane[k][sym];
       if (f == 0) {
         result = CGO_ERR_TABLE;
@@ -550,7 +660,7 @@ int64_t cgo_encode_group(const cgo_shape* s, const uint8_t* blob, const uint16_t
   const uint16_t* f_lane[64];
   group_q(s, v, X, c, l, kv, h, j, q, n);
   lane_tables(s, v, l, kv, h, j, fbuf, f_lane);
-  int64_t r = cgo_encode_group_q(q, n, f_lane, out, cap);
+  int64_t r = cgo_encode_group_q(q, n, f_lane, v->robust, out, cap);
   free(q);
   free(v);
   return r;
@@ -605,7 +715,7 @@ int64_t cgo_encode_chunk(const cgo_shape* s, const uint8_t* blob, const uint16_t
         for (int j = 0; j < slices; j++, gi++) {
           group_q(s, v, X, c, l, kv, h, j, q, n);
           lane_tables(s, v, l, kv, h, j, fbuf, f_lane);
-          int64_t m = cgo_encode_group_q(q, n, f_lane, words, bound);
+          int64_t m = cgo_encode_group_q(q, n, f_lane, v->robust, words, bound);
           if (m < 0) {
             result = m;
             goto done;
@@ -751,7 +861,7 @@ static int decode_chunk_impl(const cgo_shape* s, const uint8_t* blob, const uint
           float step = v->steps[v->lg[l]];
           for (int k = 0; k < CGO_LANES; k++)
             for (int64_t i = 0; i < n; i++) {
-              uint16_t y = cgo_dequantize(q[k * n + i], step);
+              uint16_t y = cgo_dequantize_dt(s->dtype, q[k * n + i], step);
               int64_t t = t0 + i;
               int d = 64 * j + k;
               if (pool) {

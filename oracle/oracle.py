@@ -17,6 +17,8 @@ SRC = os.path.join(HERE, "cg_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_CORRUPT, ERR_TABLE = 0, -1, -2, -3, -5, -6
+F16, BF16 = 0, 1          # element types
+TABLES_ROBUST = 1         # cgo_build_tables flag
 
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall"]
 
@@ -33,7 +35,7 @@ def build(force: bool = False) -> str:
 class Shape(ctypes.Structure):
     _fields_ = [("layers", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
-                ("tokens", ctypes.c_int64)]
+                ("tokens", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -55,10 +57,20 @@ def lib():
         L.cgo_quantize.restype = i32
         L.cgo_dequantize.argtypes = [i32, ctypes.c_float]
         L.cgo_dequantize.restype = ctypes.c_uint16
+        L.cgo_quantize_dt.argtypes = [ctypes.c_int, ctypes.c_uint16, ctypes.c_float, P, P]
+        L.cgo_quantize_dt.restype = i32
+        L.cgo_dequantize_dt.argtypes = [ctypes.c_int, i32, ctypes.c_float]
+        L.cgo_dequantize_dt.restype = ctypes.c_uint16
+        L.cgo_bf16_to_float.argtypes = [ctypes.c_uint16]
+        L.cgo_bf16_to_float.restype = ctypes.c_float
+        L.cgo_float_to_bf16.argtypes = [ctypes.c_float]
+        L.cgo_float_to_bf16.restype = ctypes.c_uint16
         L.cgo_wrap16.argtypes = [i32]
         L.cgo_wrap16.restype = i32
         L.cgo_normalize.argtypes = [P, P]
         L.cgo_normalize.restype = None
+        L.cgo_normalize_robust.argtypes = [P, P]
+        L.cgo_normalize_robust.restype = None
         L.cgo_table_counts.argtypes = [sp, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int, P, P]
         L.cgo_table_counts.restype = None
@@ -66,11 +78,11 @@ def lib():
         L.cgo_tables_f_offset.restype = u64
         L.cgo_tables_format_bytes.argtypes = [sp, i32]
         L.cgo_tables_format_bytes.restype = u64
-        L.cgo_build_tables.argtypes = [sp, i32, i32, P, P, P, P, u64, P]
+        L.cgo_build_tables.argtypes = [sp, i32, i32, P, P, P, ctypes.c_uint32, P, u64, P]
         L.cgo_build_tables.restype = ctypes.c_int
         L.cgo_group_word_bound.argtypes = [i64]
         L.cgo_group_word_bound.restype = i64
-        L.cgo_encode_group_q.argtypes = [P, i64, P, P, i64]
+        L.cgo_encode_group_q.argtypes = [P, i64, P, ctypes.c_int, P, i64]
         L.cgo_encode_group_q.restype = i64
         L.cgo_decode_group_q.argtypes = [P, i64, i64, P, P]
         L.cgo_decode_group_q.restype = ctypes.c_int
@@ -91,8 +103,13 @@ def lib():
         L.cgo_float_to_half_array.argtypes = [P, i64, P]
         L.cgo_quantize_array.argtypes = [P, i64, ctypes.c_float, P]
         L.cgo_dequantize_array.argtypes = [P, i64, ctypes.c_float, P]
+        L.cgo_bf16_to_float_array.argtypes = [P, i64, P]
+        L.cgo_float_to_bf16_array.argtypes = [P, i64, P]
+        L.cgo_quantize_array_dt.argtypes = [ctypes.c_int, P, i64, ctypes.c_float, P]
+        L.cgo_dequantize_array_dt.argtypes = [ctypes.c_int, P, i64, ctypes.c_float, P]
         for fn in ("cgo_half_to_float_array", "cgo_float_to_half_array", "cgo_quantize_array",
-                   "cgo_dequantize_array"):
+                   "cgo_dequantize_array", "cgo_bf16_to_float_array", "cgo_float_to_bf16_array",
+                   "cgo_quantize_array_dt", "cgo_dequantize_array_dt"):
             getattr(L, fn).restype = None
         _lib = L
     return _lib
@@ -103,12 +120,13 @@ def _p(a: np.ndarray):
     return ctypes.c_void_p(a.ctypes.data)
 
 
-def shape(L, H, D, T, C) -> Shape:
-    return Shape(int(L), int(H), int(D), int(C), int(T))
+def shape(L, H, D, T, C, dtype=F16) -> Shape:
+    return Shape(int(L), int(H), int(D), int(C), int(T), int(dtype), 0)
 
 
 def shape_of(cfg) -> Shape:
-    return shape(cfg.layers, cfg.kv_heads, cfg.head_dim, cfg.tokens, cfg.chunk_tokens)
+    return shape(cfg.layers, cfg.kv_heads, cfg.head_dim, cfg.tokens, cfg.chunk_tokens,
+                 getattr(cfg, "dtype", F16))
 
 
 # ---- scalar helpers ------------------------------------------------------
@@ -130,6 +148,38 @@ def dequantize(q: int, step: float) -> int:
     return lib().cgo_dequantize(int(q), float(step))
 
 
+def quantize_dt(dtype: int, h: int, step: float):
+    sat, nan_ = ctypes.c_int(0), ctypes.c_int(0)
+    q = lib().cgo_quantize_dt(int(dtype), int(h), float(step), ctypes.byref(sat), ctypes.byref(nan_))
+    return q, sat.value, nan_.value
+
+
+def dequantize_dt(dtype: int, q: int, step: float) -> int:
+    return lib().cgo_dequantize_dt(int(dtype), int(q), float(step))
+
+
+def bf16_to_float(h: int) -> float:
+    return lib().cgo_bf16_to_float(int(h))
+
+
+def float_to_bf16(f: float) -> int:
+    return lib().cgo_float_to_bf16(float(f))
+
+
+def bf16_to_float_array(h: np.ndarray) -> np.ndarray:
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, dtype=np.float32)
+    lib().cgo_bf16_to_float_array(_p(h), h.size, _p(out))
+    return out
+
+
+def float_to_bf16_array(f: np.ndarray) -> np.ndarray:
+    f = np.ascontiguousarray(f, dtype=np.float32)
+    out = np.empty(f.shape, dtype=np.uint16)
+    lib().cgo_float_to_bf16_array(_p(f), f.size, _p(out))
+    return out
+
+
 def half_to_float_array(h: np.ndarray) -> np.ndarray:
     h = np.ascontiguousarray(h, dtype=np.uint16)
     out = np.empty(h.shape, dtype=np.float32)
@@ -144,17 +194,17 @@ def float_to_half_array(f: np.ndarray) -> np.ndarray:
     return out
 
 
-def quantize_array(xh: np.ndarray, step: float) -> np.ndarray:
+def quantize_array(xh: np.ndarray, step: float, dtype: int = F16) -> np.ndarray:
     xh = np.ascontiguousarray(xh).view(np.uint16)
     out = np.empty(xh.shape, dtype=np.int32)
-    lib().cgo_quantize_array(_p(xh), xh.size, float(step), _p(out))
+    lib().cgo_quantize_array_dt(int(dtype), _p(xh), xh.size, float(step), _p(out))
     return out
 
 
-def dequantize_array(q: np.ndarray, step: float) -> np.ndarray:
+def dequantize_array(q: np.ndarray, step: float, dtype: int = F16) -> np.ndarray:
     q = np.ascontiguousarray(q, dtype=np.int32)
     out = np.empty(q.shape, dtype=np.uint16)
-    lib().cgo_dequantize_array(_p(q), q.size, float(step), _p(out))
+    lib().cgo_dequantize_array_dt(int(dtype), _p(q), q.size, float(step), _p(out))
     return out
 
 
@@ -162,11 +212,11 @@ def wrap16(v: int) -> int:
     return lib().cgo_wrap16(int(v))
 
 
-def normalize(counts) -> np.ndarray:
+def normalize(counts, robust: bool = False) -> np.ndarray:
     c = np.ascontiguousarray(counts, dtype=np.uint64)
     assert c.shape == (256,)
     f = np.zeros(256, dtype=np.uint16)
-    lib().cgo_normalize(_p(c), _p(f))
+    (lib().cgo_normalize_robust if robust else lib().cgo_normalize)(_p(c), _p(f))
     return f
 
 
@@ -179,7 +229,7 @@ def tables_f_offset(shp: Shape, n_groups: int) -> int:
     return lib().cgo_tables_f_offset(ctypes.byref(shp), n_groups)
 
 
-def build_tables(shp: Shape, level_id: int, layer_group, steps, X: np.ndarray):
+def build_tables(shp: Shape, level_id: int, layer_group, steps, X: np.ndarray, flags: int = 0):
     lg = np.ascontiguousarray(layer_group, dtype=np.uint8)
     st = np.ascontiguousarray(steps, dtype=np.float32)
     G = len(st)
@@ -187,7 +237,8 @@ def build_tables(shp: Shape, level_id: int, layer_group, steps, X: np.ndarray):
     blob = np.zeros(n, dtype=np.uint8)
     stats = np.zeros(4, dtype=np.uint64)
     rc = lib().cgo_build_tables(ctypes.byref(shp), level_id, G, _p(lg), _p(st),
-                                _p(np.ascontiguousarray(X).view(np.uint16)), _p(blob), n, _p(stats))
+                                _p(np.ascontiguousarray(X).view(np.uint16)), int(flags), _p(blob), n,
+                                _p(stats))
     if rc != OK:
         raise RuntimeError("cgo_build_tables failed: %d" % rc)
     return blob, stats
@@ -218,14 +269,15 @@ def _lane_ptrs(f_lane: np.ndarray):
     return f_lane, arr
 
 
-def encode_group_q(q: np.ndarray, f_lane: np.ndarray) -> np.ndarray:
-    """q: int32 [64][n]; f_lane: u16 [64][256]. Returns the u16 word stream."""
+def encode_group_q(q: np.ndarray, f_lane: np.ndarray, robust: bool = False) -> np.ndarray:
+    """q: int32 [64][n]; f_lane: u16 [64][256]. Returns the u16 word stream
+    (robust: symbols of frequency 0 are coded as escapes)."""
     q = np.ascontiguousarray(q, dtype=np.int32)
     n = q.shape[1]
     cap = lib().cgo_group_word_bound(n)
     out = np.zeros(cap, dtype=np.uint16)
     keep, arr = _lane_ptrs(f_lane)
-    m = lib().cgo_encode_group_q(_p(q), n, arr, _p(out), cap)
+    m = lib().cgo_encode_group_q(_p(q), n, arr, int(bool(robust)), _p(out), cap)
     if m < 0:
         raise RuntimeError("cgo_encode_group_q failed: %d" % m)
     return out[:m].copy()

@@ -56,3 +56,55 @@ def counts(X, layer_group, steps, chunk, n_groups):
             cnt[layer_group[l]] += np.bincount(idx.ravel(), minlength=2 * H * D * 256).reshape(
                 2, H, D, 256).astype(np.uint64)
     return cnt
+
+
+# ---- bfloat16 routes (torch's CPU conversions are the library routine) ----
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    import torch
+    b = np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)
+    return torch.from_numpy(b.copy()).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def f32_to_bf16_bits(f: np.ndarray) -> np.ndarray:
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(f, dtype=np.float32).copy()).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def quantize_bits(x_bits: np.ndarray, step: float, dtype: int) -> np.ndarray:
+    """quantize() for raw 16-bit element bits of either type (0 fp16, 1 bf16)."""
+    if dtype == 0:
+        return quantize(np.ascontiguousarray(x_bits, dtype=np.uint16).view(np.float16), step)
+    xf = bf16_to_f64(x_bits)
+    with np.errstate(invalid="ignore", over="ignore"):
+        v = (xf / np.float64(np.float32(step))).astype(np.float32)
+        r = np.rint(v)
+        r = np.nan_to_num(r, nan=0.0, posinf=1e9, neginf=-1e9)
+    return np.clip(r, -32768, 32767).astype(np.int64)
+
+
+def dequantize_bits(q: np.ndarray, step: float, dtype: int) -> np.ndarray:
+    if dtype == 0:
+        return dequantize(q, step).view(np.uint16)
+    with np.errstate(over="ignore"):
+        return f32_to_bf16_bits(q.astype(np.float32) * np.float32(step))
+
+
+def reconstruct_bits(X_bits, layer_group, steps, dtype):
+    return np.stack([dequantize_bits(quantize_bits(X_bits[l], steps[layer_group[l]], dtype),
+                                     steps[layer_group[l]], dtype) for l in range(X_bits.shape[0])])
+
+
+def counts_bits(X_bits, layer_group, steps, chunk, n_groups, dtype):
+    """counts() for raw element bits of either type."""
+    L, _, H, T, D = X_bits.shape
+    q = np.stack([quantize_bits(X_bits[l], steps[layer_group[l]], dtype) for l in range(L)])
+    cnt = np.zeros((n_groups, 2, H, D, 256), dtype=np.uint64)
+    for sym in symbols(q, chunk):
+        for l in range(L):
+            s = sym[l]
+            idx = ((np.arange(2)[:, None, None, None] * H + np.arange(H)[None, :, None, None]) * D
+                   + np.arange(D)[None, None, None, :]) * 256 + s
+            cnt[layer_group[l]] += np.bincount(idx.ravel(), minlength=2 * H * D * 256).reshape(
+                2, H, D, 256).astype(np.uint64)
+    return cnt
