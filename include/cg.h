@@ -12,17 +12,21 @@
  * optimisation article: physical blocks found through a block table).
  *
  * Bit-level definition (the pages leave it open; these are the readings):
+ *   x      = fp16 or bfloat16 element ("CacheGen：大语言模型推理加速的KV缓存压缩
+ *            与流式传输技术解析", 「KV缓存的量化压缩机制」: the cache is FP16/BF16)
  *   q      = clamp(round_half_even(fl32(x / step[group(layer)])), -32768, 32767), NaN -> 0
  *   d_0    = q[first token of the chunk] (raw);  d_i = wrap16(q_i - q_{i-1})
- *   symbol = d_i + 127 if |d_i| <= 127, else 255 (escape) + raw u16(d_i)
+ *   symbol = d_i + 127 if |d_i| <= 127, else 255 (escape) + raw u16(d_i);
+ *            with robust tables also 255 + raw u16(d_i) when the table gives
+ *            d_i + 127 frequency 0
  *   tables = per (layer group, K|V, head, dim) symbol counts, normalised to
  *            12-bit frequencies (sum 4096)
  *   coder  = static rANS, 32-bit state in [2^16, 2^32), 16-bit words; a group
  *            = (chunk, layer, K|V, head, 64-dim slice), lane k codes dim
  *            64*slice + k, 64 lanes interleaved word by word
- *   x_hat  = fp16_round_half_even(fl32(float(q) * step))
+ *   x_hat  = round_half_even to the element type of fl32(float(q) * step)
  *
- * Layouts (all little-endian, element = fp16 bits as uint16_t):
+ * Layouts (all little-endian, element = fp16 or bfloat16 bits as uint16_t):
  *   KV tensor  x[layer][2 (K,V)][kv_head][token][head_dim]
  *   paged pool pool[layer][2][num_blocks][kv_head][16][head_dim]
  *   tables blob, chunk record: see cg_tables_format_bytes / cg_encode.
@@ -61,6 +65,19 @@ typedef int32_t cg_status;
 #define CG_ERR_CORRUPT (-5)     /* a record or stream failed its integrity checks      */
 #define CG_ERR_TABLE (-6)       /* a symbol to encode has frequency 0 in the table     */
 
+/* Element types (cg_shape.dtype). */
+#define CG_DTYPE_F16 0
+#define CG_DTYPE_BF16 1
+
+/* cg_build_tables flags. CG_TABLES_ROBUST: tables meant for tensors other
+ * than the one they are built from (calibration data; "CacheGen：…技术解析",
+ * 「量化编码器设计」: per-channel statistics drive the coder). The escape
+ * symbol keeps a frequency of at least 1 (one unit moves to it from the
+ * largest frequency, lowest symbol on ties, when the data had no escape),
+ * and cg_encode codes a delta whose symbol has frequency 0 as an escape
+ * instead of failing with CG_ERR_TABLE. Decoding is unchanged. */
+#define CG_TABLES_ROBUST 1u
+
 /* Shape of one KV cache. head_dim must be a multiple of 64. Limits:
  * layers <= 1024, layers*tokens < 2^32, chunk_tokens <= 1<<20. */
 typedef struct cg_shape {
@@ -69,6 +86,8 @@ typedef struct cg_shape {
   int32_t head_dim;     /* D */
   int32_t chunk_tokens; /* C: delta-reset and record unit ("CacheGen实战" 2.1: 1536) */
   int64_t tokens;       /* T */
+  int32_t dtype;        /* CG_DTYPE_F16 or CG_DTYPE_BF16: elements of x, y and pool */
+  int32_t reserved;     /* 0 */
 } cg_shape;
 
 /* One quality level ("CacheGen实战" 3.1: high 0.3/0.8/1.2, balanced
@@ -110,8 +129,11 @@ size_t cg_tables_bytes(const cg_shape* shape, int32_t n_groups);
 /* Bytes of the format section alone: the part a file or another
  * implementation must reproduce. Layout: 64-byte header ("CGTB", version,
  * layers, kv_heads, head_dim, n_groups, level_id, chunk_tokens, tokens u64,
- * f_offset, 0, format_bytes u64, 0 u64), f32 step[G], u8 layer_group[L], zero
- * pad to f_offset (256-aligned), u16 f[G][2][H][D][256]. */
+ * f_offset, dtype, format_bytes u64, flags, 0), f32 step[G], u8
+ * layer_group[L], zero pad to f_offset (256-aligned), u16 f[G][2][H][D][256].
+ * Encoders and decoders take a blob only for a shape of the same layers,
+ * kv_heads, head_dim and dtype; tokens and chunk_tokens may differ (tables
+ * built on calibration data). */
 size_t cg_tables_format_bytes(const cg_shape* shape, int32_t n_groups);
 
 /* Workspace of cg_build_tables (symbol counts), or 0 for a bad shape. */
@@ -122,11 +144,12 @@ size_t cg_build_workspace_bytes(const cg_shape* shape, int32_t n_groups);
  * section 1: grouped entropy coding). Counts the symbols of tokens 1..n-1 of
  * every chunk of x_dev per (layer group, K|V, head, dim), normalises each
  * table to 12 bits and writes the blob to tables_dev (cg_tables_bytes).
+ * flags: 0 or CG_TABLES_ROBUST (other bits: CG_ERR_INVALID_ARG).
  * stats_dev (optional, u64[4]) receives {elements, saturated, nan, escapes}.
  * Data errors: none. */
 cg_status cg_build_tables(const cg_shape* shape, const cg_level* level, const uint16_t* x_dev,
-                          void* tables_dev, void* ws_dev, size_t ws_bytes, uint64_t* stats_dev,
-                          const cg_profile* prof, hipStream_t stream);
+                          void* tables_dev, void* ws_dev, size_t ws_bytes, uint32_t flags,
+                          uint64_t* stats_dev, const cg_profile* prof, hipStream_t stream);
 
 /* ---- encode -------------------------------------------------------------- */
 

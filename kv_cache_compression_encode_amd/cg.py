@@ -20,6 +20,9 @@ CG_ERR_CAPACITY = -3
 CG_ERR_HIP = -4
 CG_ERR_CORRUPT = -5
 CG_ERR_TABLE = -6
+CG_DTYPE_F16 = 0
+CG_DTYPE_BF16 = 1
+CG_TABLES_ROBUST = 1
 
 
 class CgError(RuntimeError):
@@ -31,7 +34,7 @@ class CgError(RuntimeError):
 class cg_shape(ctypes.Structure):
     _fields_ = [("layers", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
-                ("tokens", ctypes.c_int64)]
+                ("tokens", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class cg_level(ctypes.Structure):
@@ -105,8 +108,8 @@ class Level:
         self.c = cg_level(self.level_id, self.n_groups, self.lg.ctypes.data, self.steps.ctypes.data)
 
 
-def shape(layers, kv_heads, head_dim, tokens, chunk_tokens) -> cg_shape:
-    return cg_shape(int(layers), int(kv_heads), int(head_dim), int(chunk_tokens), int(tokens))
+def shape(layers, kv_heads, head_dim, tokens, chunk_tokens, dtype=CG_DTYPE_F16) -> cg_shape:
+    return cg_shape(int(layers), int(kv_heads), int(head_dim), int(chunk_tokens), int(tokens), int(dtype), 0)
 
 
 _lib = None
@@ -128,7 +131,7 @@ def lib():
         "cg_tables_bytes": (sz, [sp, i32]),
         "cg_tables_format_bytes": (sz, [sp, i32]),
         "cg_build_workspace_bytes": (sz, [sp, i32]),
-        "cg_build_tables": (i32, [sp, lp, P, P, P, sz, P, pp, P]),
+        "cg_build_tables": (i32, [sp, lp, P, P, P, sz, ctypes.c_uint32, P, pp, P]),
         "cg_encode_bound": (sz, [sp, i64, i64]),
         "cg_encode_workspace_bytes": (sz, [sp, i64, i64]),
         "cg_encode": (i32, [sp, lp, P, P, i64, i64, P, u64, P, P, sz, P, pp, P]),
@@ -205,10 +208,10 @@ def cg_build_workspace_bytes(shp: cg_shape, n_groups: int) -> int:
     return lib().cg_build_workspace_bytes(ctypes.byref(shp), n_groups)
 
 
-def cg_build_tables(shp, level: Level, x, tables, ws, stats=None, prof=None, stream=None):
+def cg_build_tables(shp, level: Level, x, tables, ws, flags=0, stats=None, prof=None, stream=None):
     rc = lib().cg_build_tables(ctypes.byref(shp), ctypes.byref(level.c), _ptr(x), _ptr(tables),
-                               _ptr(ws), ws.numel() * ws.element_size(), _ptr(stats), _prof(prof),
-                               _stream(stream))
+                               _ptr(ws), ws.numel() * ws.element_size(), int(flags), _ptr(stats),
+                               _prof(prof), _stream(stream))
     _check("cg_build_tables", rc)
 
 

@@ -8,9 +8,13 @@ import torch
 from . import cg as C
 
 
-def shape_of(cfg, tokens=None) -> C.cg_shape:
+def shape_of(cfg, tokens=None, dtype=C.CG_DTYPE_F16) -> C.cg_shape:
     return C.shape(cfg.layers, cfg.kv_heads, cfg.head_dim,
-                   cfg.tokens if tokens is None else tokens, cfg.chunk_tokens)
+                   cfg.tokens if tokens is None else tokens, cfg.chunk_tokens, dtype)
+
+
+def torch_dtype(shp) -> torch.dtype:
+    return torch.bfloat16 if shp.dtype == C.CG_DTYPE_BF16 else torch.float16
 
 
 def level_of(lv) -> C.Level:
@@ -54,11 +58,11 @@ class Codec:
     def format_bytes(self, level: C.Level) -> int:
         return C.cg_tables_format_bytes(self.shp, level.n_groups)
 
-    def build_tables(self, x: torch.Tensor, level: C.Level, tables=None, stats=None, prof=None):
+    def build_tables(self, x: torch.Tensor, level: C.Level, tables=None, stats=None, prof=None, flags=0):
         if tables is None:
             tables = _bytes(self.tables_bytes(level), self.device)
         ws = self._workspace("build", C.cg_build_workspace_bytes(self.shp, level.n_groups))
-        C.cg_build_tables(self.shp, level, x, tables, ws, stats, prof)
+        C.cg_build_tables(self.shp, level, x, tables, ws, flags, stats, prof)
         return tables
 
     # -- encode -------------------------------------------------------------
@@ -101,7 +105,7 @@ class Codec:
     def decode(self, levels, tables, refs, n_refs, y=None, prof=None):
         if y is None:
             y = torch.empty((self.shp.layers, 2, self.shp.kv_heads, self.shp.tokens, self.shp.head_dim),
-                            dtype=torch.float16, device=self.device)
+                            dtype=torch_dtype(self.shp), device=self.device)
         C.cg_decode(self.shp, levels, tables, refs, n_refs, y, self.status, prof)
         return y
 

@@ -20,7 +20,8 @@ namespace {
 cg_status check_shape(const cg_shape* sp, Shape* out) {
   if (!sp) return CG_ERR_INVALID_ARG;
   const cg_shape& s = *sp;
-  if (s.layers < 1 || s.kv_heads < 1 || s.head_dim < 1 || s.chunk_tokens < 1 || s.tokens < 1)
+  if (s.layers < 1 || s.kv_heads < 1 || s.head_dim < 1 || s.chunk_tokens < 1 || s.tokens < 1 ||
+      (s.dtype != CG_DTYPE_F16 && s.dtype != CG_DTYPE_BF16) || s.reserved != 0)
     return CG_ERR_INVALID_ARG;
   if (s.head_dim % 64 != 0) return CG_ERR_UNSUPPORTED;
   if (s.layers > kMaxLayers || s.chunk_tokens > (1 << 20) || s.kv_heads > (1 << 16) ||
@@ -39,6 +40,7 @@ cg_status check_shape(const cg_shape* sp, Shape* out) {
     out->C = s.chunk_tokens;
     out->S = s.head_dim / 64;
     out->T = s.tokens;
+    out->dt = s.dtype;
   }
   return CG_OK;
 }
@@ -257,11 +259,12 @@ size_t cg_build_workspace_bytes(const cg_shape* shape, int32_t n_groups) {
 }
 
 cg_status cg_build_tables(const cg_shape* shape, const cg_level* level, const uint16_t* x_dev,
-                          void* tables_dev, void* ws_dev, size_t ws_bytes, uint64_t* stats_dev,
-                          const cg_profile* prof, hipStream_t stream) {
+                          void* tables_dev, void* ws_dev, size_t ws_bytes, uint32_t flags,
+                          uint64_t* stats_dev, const cg_profile* prof, hipStream_t stream) {
   Shape s;
   cg_status rc = check_shape(shape, &s);
   if (rc != CG_OK) return rc;
+  if (flags & ~(uint32_t)CG_TABLES_ROBUST) return CG_ERR_INVALID_ARG;
   if ((rc = check_level(level, s)) != CG_OK) return rc;
   if (!x_dev || !tables_dev || !ws_dev || !aligned(x_dev, 2) || !aligned(tables_dev, 256) ||
       !aligned(ws_dev, 256) || (stats_dev && !aligned(stats_dev, 8)))
@@ -288,6 +291,8 @@ cg_status cg_build_tables(const cg_shape* shape, const cg_level* level, const ui
   bi.G = G;
   bi.C = s.C;
   bi.level_id = level->level_id;
+  bi.dtype = s.dt;
+  bi.flags = flags;
   bi.T = s.T;
   for (int g = 0; g < G; ++g) bi.step[g] = level->step[g];
   for (int l = 0; l < s.L; ++l) bi.lg[l] = level->layer_group[l];
@@ -298,6 +303,7 @@ cg_status cg_build_tables(const cg_shape* shape, const cg_level* level, const ui
   qa.qflags = reinterpret_cast<uint32_t*>(blob + tb_qflag_offset(s.L, s.H, s.D, G));
   qa.L = s.L;
   qa.G = G;
+  qa.bf = s.dt == kDtypeBf16;
   if ((e = launch_qcheck(qa, stream)) != hipSuccess) return CG_ERR_HIP;
 
   HistArgs ha;
@@ -318,6 +324,7 @@ cg_status cg_build_tables(const cg_shape* shape, const cg_level* level, const ui
   na.enc_off = tb_enc_offset(s.L, s.H, s.D, G);
   na.dec_off = tb_dec_offset(s.L, s.H, s.D, G);
   na.n_tables = (int64_t)ntab;
+  na.robust = (flags & CG_TABLES_ROBUST) != 0;
   return hip_status(launch_norm(na, stream));
 }
 

@@ -14,7 +14,7 @@
 //   k_fill_u32     fill (no hipMemset, so calls stay capturable)
 //   k_blob_init    tables-blob header, steps, layer groups
 //   k_qcheck       per layer group: is the 4-flop quotient exact for all 65536
-//                  fp16 inputs? (else the IEEE divide is used)
+//                  inputs of the element type? (else the IEEE divide is used)
 //   k_hist         quantize + delta + symbol, LDS-privatised 64 x 256 counts
 //   k_norm         one wavefront per table: 12-bit normalisation, cumulative
 //                  frequencies, encoder / decoder lookup tables
@@ -25,6 +25,9 @@
 //   k_write        record headers + compaction of the group streams
 //   k_decode<P>    fused rANS decode + token prefix + dequantize + store
 //                  (P: contiguous or through the block table into 16-token pages)
+// Element types: fp16 or bfloat16 (the KV cache holds either: "CacheGen：
+// 大语言模型推理加速的KV缓存压缩与流式传输技术解析", 「KV缓存的量化压缩机制」);
+// the kernels that touch elements take the type as a template parameter BF.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -76,6 +79,15 @@ __device__ __forceinline__ void set_status(int32_t* status, int32_t code) {
 // element arithmetic (bit-exact definition)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+
+// Element bits -> binary32 (exact). bfloat16 is the upper half of a binary32.
+template <bool BF>
+__device__ __forceinline__ float elem_to_f32(uint16_t h) {
+  if constexpr (BF)
+    return __uint_as_float((uint32_t)h << 16);
+  else
+    return h2f(h);
+}
 __device__ __forceinline__ uint16_t f2h(float f) { return __half_as_ushort(__float2half_rn(f)); }
 
 // (float)(int16_t)v with the sign extension folded into the conversion.
@@ -91,10 +103,10 @@ __device__ __forceinline__ float cvt_f32_sext16(int32_t v) {
 // FAST: v1 = x*r, e = x - v1*step (exact by FMA), v = v1 + e*r with r = RN(1/step);
 // used only for steps where k_qcheck proved it equal to the IEEE quotient for
 // every fp16 input. Branch-free; sat / nan_ count saturated and NaN inputs.
-template <bool FAST>
+template <bool FAST, bool BF>
 __device__ __forceinline__ int32_t quantize(uint16_t xh, float step, float rcp, uint32_t& sat,
                                             uint32_t& nan_) {
-  const float x = h2f(xh);
+  const float x = elem_to_f32<BF>(xh);
   float v;
   if (FAST) {
     const float v1 = x * rcp;
@@ -129,13 +141,21 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
   return (uint16_t)h;
 }
 
-__device__ __forceinline__ uint16_t dequantize(int32_t q, float step) {
-  return f32_to_f16_bits((float)q * step);
+// bfloat16: round to nearest even, one gfx950 conversion instruction.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+
+template <bool BF>
+__device__ __forceinline__ uint16_t f32_to_elem(float v) {
+  if constexpr (BF)
+    return f32_to_bf16_bits(v);
+  else
+    return f32_to_f16_bits(v);
 }
 
 // Same, for q held modulo 2^16 in the low half of a 32-bit register.
+template <bool BF>
 __device__ __forceinline__ uint16_t dequantize_low16(uint32_t q, float step) {
-  return f32_to_f16_bits(cvt_f32_sext16((int32_t)q) * step);
+  return f32_to_elem<BF>(cvt_f32_sext16((int32_t)q) * step);
 }
 
 // 127 + wrap16(q_t - q_{t-1}) as unsigned: below 255 it is the symbol,
@@ -180,8 +200,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 struct BlobHdr {
   uint32_t magic, version, L, H, D, G, level_id, C;
   uint64_t T;
-  uint32_t f_offset, z0;
-  uint64_t format_bytes, z1;
+  uint32_t f_offset, dtype;
+  uint64_t format_bytes;
+  uint32_t flags, z1;
 };
 
 __device__ __forceinline__ const BlobHdr* blob_hdr(const uint8_t* b) {
@@ -194,10 +215,11 @@ __device__ __forceinline__ const uint8_t* blob_lg(const uint8_t* b, int G) { ret
 __device__ __forceinline__ int layer_group(const uint8_t* b, int G, int l) {
   return uni((uint32_t)blob_lg(b, G)[l]);
 }
-__device__ __forceinline__ bool blob_ok(const uint8_t* b, int L, int H, int D, int G) {
+__device__ __forceinline__ bool blob_ok(const uint8_t* b, const Shape& s, int G) {
   const BlobHdr* bh = reinterpret_cast<const BlobHdr*>(b);
-  return uni(bh->magic) == kTableMagic && uni(bh->version) == kVersion && (int)uni(bh->L) == L &&
-         (int)uni(bh->H) == H && (int)uni(bh->D) == D && (int)uni(bh->G) == G;
+  return uni(bh->magic) == kTableMagic && uni(bh->version) == kVersion && (int)uni(bh->L) == s.L &&
+         (int)uni(bh->H) == s.H && (int)uni(bh->D) == s.D && (int)uni(bh->G) == G &&
+         (int)uni(bh->dtype) == s.dt && (uni(bh->flags) & ~kTablesRobust) == 0;
 }
 __device__ __forceinline__ bool qflag(const uint8_t* b, int L, int H, int D, int G, int g) {
   return uni(reinterpret_cast<const uint32_t*>(b + tb_qflag_offset(L, H, D, G))[g]) != 0;
@@ -274,22 +296,24 @@ __global__ void k_blob_init(BlobInitArgs a) {
     h[7] = (uint32_t)a.C;
     *reinterpret_cast<uint64_t*>(b + 32) = (uint64_t)a.T;
     h[10] = (uint32_t)foff;
-    h[11] = 0;
+    h[11] = (uint32_t)a.dtype;
     *reinterpret_cast<uint64_t*>(b + 48) = fbytes;
-    *reinterpret_cast<uint64_t*>(b + 56) = 0;
+    h[14] = a.flags;
+    h[15] = 0;
   }
   uint32_t* qf = reinterpret_cast<uint32_t*>(b + tb_qflag_offset(a.L, a.H, a.D, a.G));
   for (int g = threadIdx.x; g < 256; g += blockDim.x) qf[g] = g < a.G ? 1u : 0u;
 }
 
+template <bool BF>
 __global__ void k_qcheck(QCheckArgs a) {
   const int g = blockIdx.y;
   const uint32_t xh = blockIdx.x * blockDim.x + threadIdx.x;  // 0 .. 65535
   const float step = blob_step(a.blob, g);
   const float rcp = 1.0f / step;
   uint32_t s0 = 0, n0 = 0;
-  const int32_t qf = quantize<true>((uint16_t)xh, step, rcp, s0, n0);
-  const int32_t qi = quantize<false>((uint16_t)xh, step, rcp, s0, n0);
+  const int32_t qf = quantize<true, BF>((uint16_t)xh, step, rcp, s0, n0);
+  const int32_t qi = quantize<false, BF>((uint16_t)xh, step, rcp, s0, n0);
   if (qf != qi) atomicAnd(&a.qflags[g], 0u);
 }
 
@@ -308,7 +332,7 @@ constexpr int kHistBatch = 16;
 // Tokens [t_begin, t_end) of one (layer, K|V, head, slice) column; xr
 // covers the column from token 0 (row t at byte t * row_bytes). Every load
 // is in bounds by construction. STATS adds the saturated / NaN counts.
-template <bool FAST, bool STATS>
+template <bool FAST, bool STATS, bool BF>
 __device__ __forceinline__ void hist_range(__amdgpu_buffer_rsrc_t xr, uint32_t row_bytes, int t_begin,
                                            int t_end, int C, float step, float rcp, uint32_t* hist,
                                            int lane, uint32_t& sat, uint32_t& nan_) {
@@ -318,13 +342,13 @@ __device__ __forceinline__ void hist_range(__amdgpu_buffer_rsrc_t xr, uint32_t r
   int pos = t_begin % C;  // position of the next token inside its chunk
   if (pos != 0) {
     uint32_t d0 = 0, d1 = 0;
-    prev = quantize<FAST>(
+    prev = quantize<FAST, BF>(
         (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, (uint32_t)(t_begin - 1) * row_bytes, 0),
         step, rcp, d0, d1);
   }
   auto one = [&](uint16_t xh) {
     uint32_t s0 = 0, n0 = 0;
-    const int32_t q = quantize<FAST>(xh, step, rcp, s0, n0);
+    const int32_t q = quantize<FAST, BF>(xh, step, rcp, s0, n0);
     if (STATS) {
       sat += s0;
       nan_ += n0;
@@ -372,6 +396,7 @@ __device__ __forceinline__ void hist_range(__amdgpu_buffer_rsrc_t xr, uint32_t r
     if (t + k < t_end) one((uint16_t)xv[k]);
 }
 
+template <bool BF>
 __global__ void __launch_bounds__(kHistThreads) k_hist(HistArgs a) {
   __shared__ uint32_t hist[257 * 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -400,14 +425,14 @@ __global__ void __launch_bounds__(kHistThreads) k_hist(HistArgs a) {
   if (t_begin < t_end) {
     if (a.stats) {
       if (fast)
-        hist_range<true, true>(xr, row_bytes, t_begin, t_end, s.C, step, rcp, hist, lane, sat, nan_);
+        hist_range<true, true, BF>(xr, row_bytes, t_begin, t_end, s.C, step, rcp, hist, lane, sat, nan_);
       else
-        hist_range<false, true>(xr, row_bytes, t_begin, t_end, s.C, step, rcp, hist, lane, sat, nan_);
+        hist_range<false, true, BF>(xr, row_bytes, t_begin, t_end, s.C, step, rcp, hist, lane, sat, nan_);
     } else {
       if (fast)
-        hist_range<true, false>(xr, row_bytes, t_begin, t_end, s.C, step, rcp, hist, lane, sat, nan_);
+        hist_range<true, false, BF>(xr, row_bytes, t_begin, t_end, s.C, step, rcp, hist, lane, sat, nan_);
       else
-        hist_range<false, false>(xr, row_bytes, t_begin, t_end, s.C, step, rcp, hist, lane, sat, nan_);
+        hist_range<false, false, BF>(xr, row_bytes, t_begin, t_end, s.C, step, rcp, hist, lane, sat, nan_);
     }
   }
   __syncthreads();
@@ -492,6 +517,20 @@ __global__ void __launch_bounds__(kNormThreads) k_norm(NormArgs a) {
         S -= cut;
       }
     }
+    // robust tables: the escape (symbol 255, lane 63, k = 3) gets at least
+    // one unit, taken from the largest frequency (lowest symbol on ties)
+    if (a.robust && __shfl(f[3], 63) == 0) {
+      uint32_t bv = f[0], bi = 4 * lane;
+#pragma unroll
+      for (int k = 1; k < 4; ++k)
+        if (f[k] > bv) {
+          bv = f[k];
+          bi = 4 * lane + k;
+        }
+      wave_argmax(bv, bi);
+      if ((int)(bi >> 2) == lane) f[bi & 3] -= 1u;
+      if (lane == 63) f[3] = 1u;
+    }
     // cumulative frequencies and ranks of the present symbols
     const uint32_t fsum = f[0] + f[1] + f[2] + f[3];
     const uint32_t fex = wave_excl_scan(fsum, lane);
@@ -514,10 +553,17 @@ __global__ void __launch_bounds__(kNormThreads) k_norm(NormArgs a) {
   fv.x = f[0] | (f[1] << 16);
   fv.y = f[2] | (f[3] << 16);
   reinterpret_cast<uint2*>(fsec)[lane] = fv;
-  // encoder set: f | b << 16 per symbol
+  // encoder set: f | b << 16 | escape << 31 per symbol. The escape
+  // symbol's entry carries the flag; with robust tables a symbol of
+  // frequency 0 gets the escape's entry, so the encoder escapes it.
   uint32_t* enc = reinterpret_cast<uint32_t*>(a.blob + a.enc_off) + set * (kEncDwords * 64) + kk;
+  const uint32_t esc_entry = __shfl(f[3] | (b[3] << 16), 63) | 0x80000000u;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) enc[(4 * lane + k) * 64] = f[k] | (b[k] << 16);
+  for (int k = 0; k < 4; ++k) {
+    uint32_t e = f[k] | (b[k] << 16);
+    if (4 * lane + k == 255 || (a.robust && f[k] == 0)) e = esc_entry;
+    enc[(4 * lane + k) * 64] = e;
+  }
   // decoder set: reversed start bitmap, scaled rank bases, rank -> (d, 4096-f, b)
   uint32_t* dec = reinterpret_cast<uint32_t*>(a.blob + a.dec_off) + set * (kDecDwords * 64) + kk;
   const uint32_t w0 = bm_lds[wave][2 * lane], w1 = bm_lds[wave][2 * lane + 1];
@@ -580,28 +626,30 @@ __device__ __forceinline__ void renorm_out(uint32_t& x, uint64_t m, __amdgpu_buf
 //   S2: f of the entry, read RU(1/f)
 //   S3: escape payload, renormalisation word, state update
 struct EncTok {
-  uint32_t e;    // symbol entry f | b << 16 (S1 read)
+  uint32_t e;    // symbol entry f | b << 16 | escape << 31 (S1 read)
   uint32_t d16;  // low 16 bits: the wrapped delta, the escape payload
-  bool esc;      // this lane's delta needs an escape
+  bool esc;      // this lane codes an escape (wide delta, or robust tables)
   uint64_t me;   // lanes of the wavefront that need one
   uint32_t f;
   double r;      // RU(1/f) (S2 read)
 };
 
-template <bool FAST>
+template <bool FAST, bool BF>
 __device__ __forceinline__ void enc_s1(EncTok& k, uint16_t xprev, int32_t& qhi, float step, float rcp,
                                        const uint32_t* ftab, int lane) {
   uint32_t d0 = 0, d1 = 0;
-  const int32_t qlo = quantize<FAST>(xprev, step, rcp, d0, d1);
+  const int32_t qlo = quantize<FAST, BF>(xprev, step, rcp, d0, d1);
   k.d16 = (uint32_t)(qhi - qlo);
   const uint32_t sraw = sym_raw(qhi, qlo);
   k.e = ftab[(sraw < 255u ? sraw : 255u) * 64 + lane];
-  k.esc = sraw >= 255u;
-  k.me = __ballot(k.esc);
   qhi = qlo;
 }
 
+// the escape decision comes from the entry: symbol 255 (a wide delta) and,
+// with robust tables, every symbol of frequency 0 carry the flag
 __device__ __forceinline__ void enc_s2(EncTok& k, const double* rcp_tab, uint32_t& fmin) {
+  k.esc = (int32_t)k.e < 0;
+  k.me = __ballot(k.esc);
   k.f = k.e & 0xFFFFu;
   fmin = k.f < fmin ? k.f : fmin;
   k.r = rcp_tab[k.f];
@@ -621,13 +669,13 @@ __device__ __forceinline__ void enc_s3(const EncTok& k, uint32_t& x, uint32_t& P
   // (f = 0 only for a symbol missing from the table: the group is then
   // invalid and CG_ERR_TABLE is reported; rcp_tab[0] = 0 keeps it finite)
   const uint32_t qd = (uint32_t)((double)x * k.r);
-  x = __umul24(qd, kM - k.f) + x + (k.e >> 16);
+  x = __umul24(qd, kM - k.f) + x + ((k.e >> 16) & 0x7FFFu);
 }
 
 // Encodes tokens n-1 .. 1 of a group (backward), then the head. xr covers the
 // group's column of x (row t at byte t * row_bytes), sr its scratch slot of
 // cap words; every access is in bounds by construction.
-template <bool FAST>
+template <bool FAST, bool BF>
 __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, uint32_t row_bytes,
                                              float step, float rcp, const uint32_t* ftab,
                                              const double* rcp_tab, __amdgpu_buffer_rsrc_t sr,
@@ -639,14 +687,14 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
   uint32_t fmin = 0xFFFFFFFFu;
   auto row = [&](int r) { return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, (uint32_t)r * row_bytes, 0); };
   uint32_t d0 = 0, d1 = 0;
-  int32_t qhi = quantize<FAST>(row(n - 1), step, rcp, d0, d1);
+  int32_t qhi = quantize<FAST, BF>(row(n - 1), step, rcp, d0, d1);
   if (n >= 3) {
     // a: token in S3, b: in S2, c: in S1. Prologue: token n-1 through S1 and
     // S2, token n-2 through S1.
     EncTok a, b, c;
-    enc_s1<FAST>(a, row(n - 2), qhi, step, rcp, ftab, lane);
+    enc_s1<FAST, BF>(a, row(n - 2), qhi, step, rcp, ftab, lane);
     enc_s2(a, rcp_tab, fmin);
-    enc_s1<FAST>(b, row(n - 3), qhi, step, rcp, ftab, lane);
+    enc_s1<FAST, BF>(b, row(n - 3), qhi, step, rcp, ftab, lane);
     // tokens i, i-1, ... enter S1 with x of rows i-1, i-2, ...; the rows of
     // the next batch are loaded while the current one is encoded. Offsets
     // stay scalar: a batch of 16 rows all >= 0 needs no clamp; the last one
@@ -670,7 +718,7 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
     load_batch(xv, i);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // as in hist_range
     auto advance = [&](uint16_t xprev) {
-      enc_s1<FAST>(c, xprev, qhi, step, rcp, ftab, lane);
+      enc_s1<FAST, BF>(c, xprev, qhi, step, rcp, ftab, lane);
       enc_s2(b, rcp_tab, fmin);
       enc_s3(a, x, P, sr);
       a = b;
@@ -693,7 +741,7 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
     enc_s3(b, x, P, sr);
   } else if (n == 2) {
     EncTok a;
-    enc_s1<FAST>(a, row(0), qhi, step, rcp, ftab, lane);
+    enc_s1<FAST, BF>(a, row(0), qhi, step, rcp, ftab, lane);
     enc_s2(a, rcp_tab, fmin);
     enc_s3(a, x, P, sr);
   }
@@ -740,6 +788,7 @@ __device__ __forceinline__ int layers_in_group(const uint8_t* blob, int G, int L
 constexpr int kEncRcpBytes = 8 * (kM + 1);
 constexpr int kEncFtabOff = (kEncRcpBytes + 255) / 256 * 256;
 
+template <bool BF>
 __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
   __shared__ __align__(16) uint8_t enc_lds[kEncFtabOff + 4 * kEncDwords * 64];
   double* rcp_tab = reinterpret_cast<double*>(enc_lds);
@@ -765,7 +814,7 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
     cl_end = cl_begin + a.chunks_per_block2 < a.n_chunks ? cl_begin + a.chunks_per_block2 : a.n_chunks;
   }
   const int G = a.G;
-  if (!blob_ok(a.blob, s.L, s.H, s.D, G)) {
+  if (!blob_ok(a.blob, s, G)) {
     if (tid == 0) set_status(a.status, CG_ERR_INVALID_ARG);
     return;
   }
@@ -804,10 +853,10 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(xb, (uint32_t)n * row_bytes);
     uint32_t words, start;
     if (fast)
-      encode_group<true>(xr, (int)n, row_bytes, step, rcp, ftab, rcp_tab, sr, cap, lane, words, start,
+      encode_group<true, BF>(xr, (int)n, row_bytes, step, rcp, ftab, rcp_tab, sr, cap, lane, words, start,
                          table_err);
     else
-      encode_group<false>(xr, (int)n, row_bytes, step, rcp, ftab, rcp_tab, sr, cap, lane, words, start,
+      encode_group<false, BF>(xr, (int)n, row_bytes, step, rcp, ftab, rcp_tab, sr, cap, lane, words, start,
                           table_err);
     if (lane == 0) {
       a.group_words[slot] = words;
@@ -1108,7 +1157,7 @@ __device__ __forceinline__ uint32_t stream_load(const Chain& c, uint32_t wbase, 
 
 // Sets up one group: checks its directory entry, stages its first 256 words,
 // reads the head and writes token 0. c.ok = false for a damaged entry.
-template <bool PAGED>
+template <bool PAGED, bool BF>
 __device__ __forceinline__ void chain_open(const DecodeArgs& a, Chain& c, const GroupRef& gr,
                                            int64_t gpc, int kv, int h, int j, float step,
                                            uint16_t* ring, int lane) {
@@ -1157,7 +1206,7 @@ __device__ __forceinline__ void chain_open(const DecodeArgs& a, Chain& c, const 
     c.bt1 = i1 <= last ? (uint32_t)a.block_table[i1] : 0u;
   }
   c.doff = row_offset<PAGED>(a, c, gr.t0, h, row_bytes, lane);
-  __builtin_amdgcn_raw_buffer_store_b16(dequantize_low16(c.q, step), c.dst, 2u * lane, c.doff, 0);
+  __builtin_amdgcn_raw_buffer_store_b16(dequantize_low16<BF>(c.q, step), c.dst, 2u * lane, c.doff, 0);
 }
 
 __device__ __forceinline__ void chain_close(const DecodeArgs& a, const Chain& c, int lane) {
@@ -1166,7 +1215,7 @@ __device__ __forceinline__ void chain_close(const DecodeArgs& a, const Chain& c,
 }
 
 // Tokens [i_begin, i_end) of NC chains in lockstep.
-template <bool PAGED, int NC>
+template <bool PAGED, int NC, bool BF>
 __device__ __forceinline__ void chain_steps(const DecodeArgs& a, Chain* c, int i_begin, int i_end,
                                             const uint32_t* tabs, int h, float step, int lane) {
   const uint32_t lane4 = 4u * lane, lane2 = 2u * lane;
@@ -1246,7 +1295,7 @@ __device__ __forceinline__ void chain_steps(const DecodeArgs& a, Chain* c, int i
     }
 #pragma unroll
     for (int k = 0; k < NC; ++k) {
-      const uint16_t y = dequantize_low16(c[k].q, step);
+      const uint16_t y = dequantize_low16<BF>(c[k].q, step);
       if (PAGED)
         c[k].doff = row_offset<PAGED>(a, c[k], c[k].t0 + i, h, row_bytes, lane);
       else
@@ -1341,7 +1390,7 @@ __device__ __forceinline__ void ph_c(Chain& c) {
   c.w = rp[mbcnt_base(c.mr, 0)];  // every lane reads; only renormalising lanes use it
 }
 
-template <bool PAGED>
+template <bool PAGED, bool BF>
 __device__ __forceinline__ void ph_d(const DecodeArgs& a, Chain& c, int i, int h, float step,
                                      uint32_t row_bytes, int lane) {
   renorm_lanes(c.x, c.w, c.mr);
@@ -1354,7 +1403,7 @@ __device__ __forceinline__ void ph_d(const DecodeArgs& a, Chain& c, int i, int h
     if ((c.info & 0xFFu) == 0x80u) c.q += 128u + ep[mbcnt_base(me, 0)];
     add_twice(c.pb, (uint32_t)__popcll(me));
   }
-  const uint16_t y = dequantize_low16(c.q, step);
+  const uint16_t y = dequantize_low16<BF>(c.q, step);
   if (PAGED)
     c.doff = row_offset<PAGED>(a, c, c.t0 + i, h, row_bytes, lane);
   else
@@ -1367,7 +1416,7 @@ __device__ __forceinline__ void ph_d(const DecodeArgs& a, Chain& c, int i, int h
 // Tokens [i0, i1) of NC = 2 or 3 chains, i1 > i0, software-pipelined. A
 // scheduling fence after every phase keeps each phase's LDS read where it is
 // issued (the compiler would sink the reads to the end of a slot).
-template <bool PAGED, int NC>
+template <bool PAGED, int NC, bool BF>
 __device__ __forceinline__ void chain_pipe(const DecodeArgs& a, Chain* c, int i0, int i1,
                                            const uint32_t* tabs, int h, float step, int lane) {
   static_assert(NC == 2 || NC == 3, "two or three chains");
@@ -1399,7 +1448,7 @@ __device__ __forceinline__ void chain_pipe(const DecodeArgs& a, Chain* c, int i0
   }
   int it = 1;
   for (int i = i0; i < i1 - 1; ++i, ++it) {
-    ph_d<PAGED>(a, c[0], i, h, step, row_bytes, lane);
+    ph_d<PAGED, BF>(a, c[0], i, h, step, row_bytes, lane);
     ph_a<NC>(c[0], tabs, lane, it);
     CG_SLOT;
     ph_c(c[1]);
@@ -1410,7 +1459,7 @@ __device__ __forceinline__ void chain_pipe(const DecodeArgs& a, Chain* c, int i0
     }
     ph_b(c[0], tabs);
     CG_SLOT;
-    ph_d<PAGED>(a, c[1], i, h, step, row_bytes, lane);
+    ph_d<PAGED, BF>(a, c[1], i, h, step, row_bytes, lane);
     ph_a<NC>(c[1], tabs, lane, it);
     CG_SLOT;
     if (NC == 3) {
@@ -1422,19 +1471,19 @@ __device__ __forceinline__ void chain_pipe(const DecodeArgs& a, Chain* c, int i0
     ph_b(c[1], tabs);
     CG_SLOT;
     if (NC == 3) {
-      ph_d<PAGED>(a, c[2], i, h, step, row_bytes, lane);
+      ph_d<PAGED, BF>(a, c[2], i, h, step, row_bytes, lane);
       ph_a<NC>(c[2], tabs, lane, it);
       CG_SLOT;
     }
   }
   // epilogue: finish token i1 - 1
-  ph_d<PAGED>(a, c[0], i1 - 1, h, step, row_bytes, lane);
+  ph_d<PAGED, BF>(a, c[0], i1 - 1, h, step, row_bytes, lane);
   ph_c(c[1]);
   if (NC == 3) ph_b(c[2], tabs);
-  ph_d<PAGED>(a, c[1], i1 - 1, h, step, row_bytes, lane);
+  ph_d<PAGED, BF>(a, c[1], i1 - 1, h, step, row_bytes, lane);
   if (NC == 3) {
     ph_c(c[2]);
-    ph_d<PAGED>(a, c[2], i1 - 1, h, step, row_bytes, lane);
+    ph_d<PAGED, BF>(a, c[2], i1 - 1, h, step, row_bytes, lane);
   }
   // the last prefetches may still be in flight into registers the compiler
   // considers free from here on
@@ -1445,27 +1494,27 @@ __device__ __forceinline__ void chain_pipe(const DecodeArgs& a, Chain* c, int i0
 
 // NC chains decoded together for their common length, then the longer ones
 // finish one at a time.
-template <bool PAGED, int NC>
+template <bool PAGED, int NC, bool BF>
 __device__ __forceinline__ void run_chains(const DecodeArgs& a, Chain* c, const uint32_t* tabs,
                                            int h, float step, int lane) {
   int nmin = c[0].n;
 #pragma unroll
   for (int k = 1; k < NC; ++k) nmin = c[k].n < nmin ? c[k].n : nmin;
   if constexpr (NC == 1) {
-    chain_steps<PAGED, 1>(a, c, 1, nmin, tabs, h, step, lane);
+    chain_steps<PAGED, 1, BF>(a, c, 1, nmin, tabs, h, step, lane);
   } else {
-    if (nmin > 1) chain_pipe<PAGED, NC>(a, c, 1, nmin, tabs, h, step, lane);
+    if (nmin > 1) chain_pipe<PAGED, NC, BF>(a, c, 1, nmin, tabs, h, step, lane);
   }
   if constexpr (NC > 1) {
 #pragma unroll
     for (int k = 0; k < NC; ++k)
-      if (c[k].n > nmin) chain_steps<PAGED, 1>(a, &c[k], nmin > 1 ? nmin : 1, c[k].n, tabs, h, step, lane);
+      if (c[k].n > nmin) chain_steps<PAGED, 1, BF>(a, &c[k], nmin > 1 ? nmin : 1, c[k].n, tabs, h, step, lane);
   }
 #pragma unroll
   for (int k = 0; k < NC; ++k) chain_close(a, c[k], lane);
 }
 
-template <bool PAGED>
+template <bool PAGED, bool BF>
 __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
   __shared__ uint32_t tabs[kDecDwords * 64];
   __shared__ uint16_t rings[kWaves * kChains * kRingStride];
@@ -1500,7 +1549,7 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
   const int G = a.n_groups[ti];
   if (g >= G) return;
   const uint8_t* blob = a.tables[ti];
-  if (!blob_ok(blob, s.L, s.H, s.D, G) ||
+  if (!blob_ok(blob, s, G) ||
       (int32_t)uni(blob_hdr(blob)->level_id) != a.level_id[ti]) {
     if (tid == 0) set_status(a.status, CG_ERR_INVALID_ARG);
     return;
@@ -1585,7 +1634,7 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
       const int ri = it / lg_count;
       GroupRef gr = ri == 0 ? rr0 : ri == 1 ? rr1 : rr2;
       gr.l = layer_of_group(blob, G, s.L, g, it - ri * lg_count, lane);
-      chain_open<PAGED>(a, c[k], gr, gpc, kv, h, j, step, rings + (wave * kChains + k) * kRingStride,
+      chain_open<PAGED, BF>(a, c[k], gr, gpc, kv, h, j, step, rings + (wave * kChains + k) * kRingStride,
                         lane);
     } else {
       c[k].ok = false;
@@ -1593,14 +1642,14 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
   }
   const bool all_ok = c[0].ok && (mine < 2 || c[1].ok) && (mine < 3 || c[2].ok);
   if (all_ok && mine == 3) {
-    run_chains<PAGED, 3>(a, c, tabs, h, step, lane);
+    run_chains<PAGED, 3, BF>(a, c, tabs, h, step, lane);
   } else if (all_ok && mine == 2) {
-    run_chains<PAGED, 2>(a, c, tabs, h, step, lane);
+    run_chains<PAGED, 2, BF>(a, c, tabs, h, step, lane);
   } else {
     // one chain, or a damaged directory entry among them: the rest one by one
 #pragma unroll
     for (int k = 0; k < kChains; ++k)
-      if (c[k].ok) run_chains<PAGED, 1>(a, &c[k], tabs, h, step, lane);
+      if (c[k].ok) run_chains<PAGED, 1, BF>(a, &c[k], tabs, h, step, lane);
   }
 }
 
@@ -1646,13 +1695,19 @@ hipError_t launch_blob_init(const BlobInitArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_qcheck(const QCheckArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_qcheck, dim3(65536 / 256, a.G), dim3(256), 0, st, a);
+  if (a.bf)
+    hipLaunchKernelGGL(k_qcheck<true>, dim3(65536 / 256, a.G), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_qcheck<false>, dim3(65536 / 256, a.G), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_hist(const HistArgs& a, hipStream_t st) {
   const uint64_t blocks = (uint64_t)a.s.L * 2 * a.s.H * a.s.S;
-  hipLaunchKernelGGL(k_hist, dim3((unsigned)blocks), dim3(kHistThreads), 0, st, a);
+  if (a.s.dt == kDtypeBf16)
+    hipLaunchKernelGGL(k_hist<true>, dim3((unsigned)blocks), dim3(kHistThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_hist<false>, dim3((unsigned)blocks), dim3(kHistThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1666,7 +1721,10 @@ hipError_t launch_encode(const EncodeArgs& a, hipStream_t st) {
   const uint64_t rblocks = (uint64_t)(a.split / a.chunks_per_block) +
                            (uint64_t)(a.n_chunks - a.split + a.chunks_per_block2 - 1) / a.chunks_per_block2;
   const uint64_t blocks = rblocks * a.G * 2 * a.s.H * a.s.S;
-  hipLaunchKernelGGL(k_encode, dim3((unsigned)blocks), dim3(kEncThreads), 0, st, a);
+  if (a.s.dt == kDtypeBf16)
+    hipLaunchKernelGGL(k_encode<true>, dim3((unsigned)blocks), dim3(kEncThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_encode<false>, dim3((unsigned)blocks), dim3(kEncThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1690,10 +1748,15 @@ hipError_t launch_decode(const DecodeArgs& a, bool paged, hipStream_t st) {
   const uint64_t rblocks = (uint64_t)(a.split / a.refs_per_block) +
                            (uint64_t)(a.n_refs - a.split + a.refs_per_block2 - 1) / a.refs_per_block2;
   const uint64_t blocks = rblocks * a.g_max * 2 * a.s.H * a.s.S;
-  if (paged)
-    hipLaunchKernelGGL(k_decode<true>, dim3((unsigned)blocks), dim3(kDecThreads), 0, st, a);
+  const bool bf = a.s.dt == kDtypeBf16;
+  if (paged && bf)
+    hipLaunchKernelGGL((k_decode<true, true>), dim3((unsigned)blocks), dim3(kDecThreads), 0, st, a);
+  else if (paged)
+    hipLaunchKernelGGL((k_decode<true, false>), dim3((unsigned)blocks), dim3(kDecThreads), 0, st, a);
+  else if (bf)
+    hipLaunchKernelGGL((k_decode<false, true>), dim3((unsigned)blocks), dim3(kDecThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(k_decode<false>, dim3((unsigned)blocks), dim3(kDecThreads), 0, st, a);
+    hipLaunchKernelGGL((k_decode<false, false>), dim3((unsigned)blocks), dim3(kDecThreads), 0, st, a);
   return hipGetLastError();
 }
 

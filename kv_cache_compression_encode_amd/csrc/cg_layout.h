@@ -11,6 +11,8 @@ namespace cg {
 constexpr uint32_t kTableMagic = 0x42544743u;   // "CGTB"
 constexpr uint32_t kRecordMagic = 0x4B434743u;  // "CGCK"
 constexpr uint32_t kVersion = 1;
+constexpr int kDtypeF16 = 0, kDtypeBf16 = 1;  // element types (shape.dtype)
+constexpr uint32_t kTablesRobust = 1u;        // tables flag: unseen symbols escape
 constexpr int kLanes = 64;           // channels per group = wavefront width
 constexpr int kHdrWords = 192;       // state hi, state lo, raw q0: 3 x 64 words
 constexpr uint32_t kM = 4096;        // 12-bit frequency total
@@ -99,6 +101,7 @@ __host__ __device__ inline uint64_t group_cap_words(int64_t n) {
 struct Shape {
   int L, H, D, C, S;  // S = D / 64 slices
   int64_t T;
+  int dt;             // kDtypeF16 or kDtypeBf16
 };
 
 // ---- launch arguments --------------------------------------------------------
@@ -106,6 +109,8 @@ struct BlobInitArgs {
   uint8_t* blob;
   int L, H, D, G, C;
   int32_t level_id;
+  int32_t dtype;
+  uint32_t flags;
   int64_t T;
   float step[kMaxGroups + 1];
   uint8_t lg[kMaxLayers];
@@ -115,6 +120,7 @@ struct QCheckArgs {
   const uint8_t* blob;
   uint32_t* qflags;
   int L, G;
+  bool bf;  // inputs are bfloat16
 };
 
 struct HistArgs {
@@ -131,6 +137,7 @@ struct NormArgs {
   uint8_t* blob;
   uint64_t f_off, enc_off, dec_off;
   int64_t n_tables;
+  bool robust;  // kTablesRobust
 };
 
 struct EncodeArgs {

@@ -16,8 +16,9 @@ def need_gpu():
     C.lib()  # fails loudly when libcg.so is missing
 
 
-def to_dev(X):
-    return torch.from_numpy(np.ascontiguousarray(X).view(np.int16)).to("cuda").view(torch.float16)
+def to_dev(X, dtype=0):
+    t = torch.from_numpy(np.ascontiguousarray(X).view(np.int16)).to("cuda")
+    return t.view(torch.bfloat16 if dtype == 1 else torch.float16)
 
 
 def u8(t):
@@ -25,13 +26,19 @@ def u8(t):
         t.detach().cpu().contiguous().view(torch.uint8).numpy()
 
 
-def gpu_roundtrip(L, H, D, T, Cc, lg, steps, X, level_id=1):
-    shp = C.shape(L, H, D, T, Cc)
+def gpu_roundtrip(L, H, D, T, Cc, lg, steps, X, level_id=1, dtype=0, flags=0, X_tables=None):
+    """X_tables: tables from this tensor (same L, H, D; any token count)
+    instead of X, e.g. calibration data for robust tables."""
+    shp = C.shape(L, H, D, T, Cc, dtype)
     lv = C.Level(level_id, lg, steps)
     cd = codec.Codec(shp)
-    x = to_dev(X)
+    x = to_dev(X, dtype)
     stats = torch.zeros(4, dtype=torch.int64, device="cuda")
-    tables = cd.build_tables(x, lv, stats=stats)
+    if X_tables is None:
+        tables = cd.build_tables(x, lv, stats=stats, flags=flags)
+    else:
+        cshp = C.shape(L, H, D, X_tables.shape[3], Cc, dtype)
+        tables = codec.Codec(cshp).build_tables(to_dev(X_tables, dtype), lv, stats=stats, flags=flags)
     out, offs = cd.encode(x, lv, tables)
     st_enc = cd.read_status()
     refs, n = cd.refs_for(out, offs)
@@ -41,9 +48,13 @@ def gpu_roundtrip(L, H, D, T, Cc, lg, steps, X, level_id=1):
                 y=y, st_enc=st_enc, st_dec=st_dec)
 
 
-def oracle_roundtrip(L, H, D, T, Cc, lg, steps, X, level_id=1):
-    oshp = O.shape(L, H, D, T, Cc)
-    blob, stats = O.build_tables(oshp, level_id, lg, steps, X)
+def oracle_roundtrip(L, H, D, T, Cc, lg, steps, X, level_id=1, dtype=0, flags=0, X_tables=None):
+    oshp = O.shape(L, H, D, T, Cc, dtype)
+    if X_tables is None:
+        blob, stats = O.build_tables(oshp, level_id, lg, steps, X, flags=flags)
+    else:
+        cshp = O.shape(L, H, D, X_tables.shape[3], Cc, dtype)
+        blob, stats = O.build_tables(cshp, level_id, lg, steps, X_tables, flags=flags)
     data, offs = O.encode_all(oshp, blob, X)
     Y = O.decode_all(oshp, blob, data, offs)
     return dict(shp=oshp, blob=blob, stats=stats, data=data, offs=offs, Y=Y)

@@ -1,0 +1,125 @@
+"""GPU path against the oracle for bfloat16 elements and robust calibration
+tables ("CacheGen：…技术解析", 「KV缓存的量化压缩机制」: FP16/BF16 caches;
+「量化编码器设计」: per-channel statistics, here taken from other data).
+Tables, records and decoded elements are compared byte by byte."""
+import numpy as np
+import pytest
+
+from kv_cache_compression_encode_amd import synth
+
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+BF16, ROBUST = 1, 1
+
+
+def all_bf16_patterns():
+    """[1][2][1][1024][64]: K holds every bf16 bit pattern once, V the same
+    patterns in reverse order."""
+    k = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(1024, 64)
+    return np.stack([k, k[::-1, ::-1]])[None, :, None].copy()
+
+
+CASES = [
+    # name, L, H, D, T, C, layer_group, steps, dtype, flags, X, X_tables
+    ("bf16-ar1", 3, 2, 128, 700, 256, [0, 1, 1], [0.5, 1.5], BF16, 0,
+     lambda: synth.random_kv_bf16(3, 2, 128, 700, 31), None),
+    ("bf16-wide-range", 2, 1, 64, 300, 100, [0, 1], [2e5, 7e5], BF16, 0,
+     lambda: synth.random_kv_bf16(2, 1, 64, 300, 32, scale=1e6), None),
+    ("bf16-every-pattern", 1, 1, 64, 1024, 256, [0], [0.37], BF16, 0, all_bf16_patterns, None),
+    ("robust-fp16", 3, 2, 64, 500, 128, [0, 1, 2], [0.5, 1.0, 1.5], 0, ROBUST,
+     lambda: synth.random_kv(3, 2, 64, 500, 33, scale=8.0, rho=0.5),
+     lambda: synth.random_kv(3, 2, 64, 260, 34, scale=1.0, rho=0.99)),
+    ("robust-bf16", 2, 2, 128, 400, 150, [0, 1], [0.3, 1.2], BF16, ROBUST,
+     lambda: synth.random_kv_bf16(2, 2, 128, 400, 35, scale=20.0, rho=0.6),
+     lambda: synth.random_kv_bf16(2, 2, 128, 333, 36, scale=2.0, rho=0.99)),
+    ("robust-self", 2, 1, 64, 200, 64, [0, 0], [0.8], 0, ROBUST,
+     lambda: synth.random_kv(2, 1, 64, 200, 37), None),
+]
+
+
+@pytest.fixture(scope="module", params=CASES, ids=[c[0] for c in CASES])
+def pair(request):
+    U.need_gpu()
+    name, L, H, D, T, Cc, lg, steps, dt, fl, mk, mk_t = request.param
+    X = mk()
+    Xt = mk_t() if mk_t else None
+    print("case", name, flush=True)
+    args = (L, H, D, T, Cc, lg, steps, X, 9)
+    kw = dict(dtype=dt, flags=fl, X_tables=Xt)
+    return U.gpu_roundtrip(*args, **kw), U.oracle_roundtrip(*args, **kw)
+
+
+def test_tables_bit_exact(pair):
+    g, o = pair
+    fb = len(o["blob"])
+    assert np.array_equal(U.u8(g["tables"])[:fb], o["blob"])
+
+
+def test_stats_exact(pair):
+    g, o = pair
+    assert np.array_equal(g["stats"].cpu().numpy().astype(np.uint64), o["stats"])
+
+
+def test_records_bit_exact(pair):
+    g, o = pair
+    assert g["st_enc"] == 0
+    offs = g["offs"].cpu().numpy().astype(np.uint64)
+    assert np.array_equal(offs, o["offs"])
+    assert np.array_equal(U.u8(g["out"])[:int(offs[-1])], o["data"])
+
+
+def test_decode_bit_exact(pair):
+    g, o = pair
+    assert g["st_dec"] == 0
+    assert np.array_equal(g["y"].cpu().view(U.torch.int16).numpy().view(np.uint16), o["Y"])
+
+
+def test_plain_tables_refuse_unseen_symbols():
+    """Without the flag, the calibration tables cannot code the other tensor:
+    CG_ERR_TABLE, as in the oracle."""
+    U.need_gpu()
+    X = synth.random_kv(3, 2, 64, 500, 33, scale=8.0, rho=0.5)
+    Xt = synth.random_kv(3, 2, 64, 260, 34, scale=1.0, rho=0.99)
+    g = U.gpu_roundtrip(3, 2, 64, 500, 128, [0, 1, 2], [0.5, 1.0, 1.5], X, 9, X_tables=Xt)
+    assert g["st_enc"] == U.C.CG_ERR_TABLE
+
+
+def test_dtype_mismatch_rejected():
+    """A bf16 tables blob used with an fp16 shape: CG_ERR_INVALID_ARG from the
+    encoder's blob check."""
+    U.need_gpu()
+    torch = U.torch
+    Xb = synth.random_kv_bf16(1, 1, 64, 64, 38)
+    shp_b = U.C.shape(1, 1, 64, 64, 32, BF16)
+    lv = U.C.Level(2, [0], [0.5])
+    tables = U.codec.Codec(shp_b).build_tables(U.to_dev(Xb, BF16), lv)
+    cd16 = U.codec.Codec(U.C.shape(1, 1, 64, 64, 32, 0))
+    cd16.encode(U.to_dev(Xb, 0), lv, tables)
+    assert cd16.read_status() == U.C.CG_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+
+
+def test_paged_bf16_matches_oracle():
+    U.need_gpu()
+    torch = U.torch
+    L, H, D, T, Cc = 2, 2, 64, 333, 128
+    X = synth.random_kv_bf16(L, H, D, T, 39)
+    args = (L, H, D, T, Cc, [0, 1], [0.5, 1.0], X, 9)
+    g = U.gpu_roundtrip(*args, dtype=BF16)
+    o = U.oracle_roundtrip(*args, dtype=BF16)
+    nb = -(-T // 16) + 5
+    bt = np.random.default_rng(40).permutation(nb)[: -(-T // 16)].astype(np.int32)
+    pool = torch.zeros((L, 2, nb, H, 16, D), dtype=torch.bfloat16, device="cuda")
+    cd = g["cd"]
+    refs, n = cd.refs_for(g["out"], g["offs"])
+    cd.decode_paged([g["lv"]], [g["tables"]], refs, n, pool, torch.from_numpy(bt).to("cuda"))
+    assert cd.read_status() == 0
+    opool = np.zeros((L, 2, nb, H, 16, D), dtype=np.uint16)
+    from oracle import oracle as O
+    offs = o["offs"]
+    for c in range(len(offs) - 1):
+        assert O.decode_chunk_paged(o["shp"], o["blob"], o["data"][int(offs[c]):int(offs[c + 1])],
+                                    opool, bt) == 0
+    assert np.array_equal(pool.cpu().view(torch.int16).numpy().view(np.uint16), opool)
