@@ -9,6 +9,11 @@ tables), cg_encode (interleaved rANS + record compaction) and cg_decode
 value = fp16 bytes of the KV cache / seconds per step (round trip). The JSON
 line also carries decode / encode / table-build GB/s, the compression ratio,
 the roofline of the dominant kernel and the CPU oracle timed on a sample.
+
+Variants (their own lines, not the headline): --dtype bf16 runs the same
+workload as bfloat16 elements (the fp16 draw rounded to bfloat16);
+--robust builds robust tables from the first quarter of the tokens only
+(calibration data) and encodes the whole cache with them.
 """
 from __future__ import annotations
 
@@ -29,9 +34,10 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(cfg, X, seconds=10.0):
+def cpu_baseline(cfg, X, seconds=10.0, dtype=0, flags=0):
     """The oracle (single thread) on a bounded sample of the same workload:
-    layer 0, all heads, the first two chunks; build + encode + decode."""
+    layer 0, all heads, the first two chunks; build + encode + decode.
+    X: element bits (uint16) of the workload."""
     import numpy as np
 
     from oracle import oracle as O
@@ -39,13 +45,13 @@ def cpu_baseline(cfg, X, seconds=10.0):
     lvd = cfg.levels[0]
     T = min(cfg.tokens, 2 * cfg.chunk_tokens)
     Xs = np.ascontiguousarray(X[:1, :, :, :T, :])
-    shp = O.shape(1, cfg.kv_heads, cfg.head_dim, T, cfg.chunk_tokens)
+    shp = O.shape(1, cfg.kv_heads, cfg.head_dim, T, cfg.chunk_tokens, dtype)
     steps = [lvd.steps[lvd.layer_group[0]]]
     elems = 0
     t0 = time.perf_counter()
     reps = 0
     while True:
-        blob, _ = O.build_tables(shp, lvd.level_id, [0], steps, Xs)
+        blob, _ = O.build_tables(shp, lvd.level_id, [0], steps, Xs, flags=flags)
         data, offs = O.encode_all(shp, blob, Xs)
         O.decode_all(shp, blob, data, offs)
         elems += Xs.size
@@ -69,6 +75,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="per-launch HBM bytes of the kernels from rocprofv3 counters")
+    ap.add_argument("--dtype", choices=("fp16", "bf16"), default="fp16")
+    ap.add_argument("--robust", action="store_true",
+                    help="robust tables from the first quarter of the tokens")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed steps, one library copy of this many bytes (the calibration "
                          "launch for the FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -93,12 +102,23 @@ def main():
     log("generated %s %s in %.1f s" % (cfg.name, X.shape, time.perf_counter() - t_gen))
     dev = torch.device("cuda:0")
     x = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.float16)
+    bf = args.dtype == "bf16"
+    if bf:
+        x = x.to(torch.bfloat16)
     N = x.numel()
     fp16_bytes = 2 * N
 
-    shp = codec.shape_of(cfg)
+    dt = C.CG_DTYPE_BF16 if bf else C.CG_DTYPE_F16
+    shp = codec.shape_of(cfg, dtype=dt)
     lv = codec.level_of(lvd)
     cd = codec.Codec(shp, dev)
+    flags = C.CG_TABLES_ROBUST if args.robust else 0
+    if args.robust:
+        t_cal = cfg.tokens // 4
+        x_tab = x[:, :, :, :t_cal, :].contiguous()
+        cd_tab = codec.Codec(codec.shape_of(cfg, tokens=t_cal, dtype=dt), dev)
+    else:
+        x_tab, cd_tab = x, cd
     nch = codec.n_chunks(shp)
     tables = torch.empty(cd.tables_bytes(lv), dtype=torch.uint8, device=dev)
     out = torch.empty(C.cg_encode_bound(shp, 0, nch), dtype=torch.uint8, device=dev)
@@ -111,7 +131,7 @@ def main():
         kt = kt or {}
         if ev:
             ev[0].record(stream)
-        cd.build_tables(x, lv, tables=tables, prof=kt.get("build"))
+        cd_tab.build_tables(x_tab, lv, tables=tables, prof=kt.get("build"), flags=flags)
         if ev:
             ev[1].record(stream)
         cd.encode(x, lv, tables, out=out, offsets=offs, prof=kt.get("encode"))
@@ -175,12 +195,13 @@ def main():
     for _ in range(4):
         l, kv, h = int(rng.integers(cfg.layers)), int(rng.integers(2)), int(rng.integers(cfg.kv_heads))
         step_ = np.float32(lvd.steps[lvd.layer_group[l]])
-        xs = X[l, kv, h].astype(np.float64)
+        xs = x[l, kv, h].cpu().to(torch.float64).numpy()
         with np.errstate(all="ignore"):
             q = np.clip(np.rint((xs / np.float64(step_)).astype(np.float32)), -32768, 32767)
             q = np.nan_to_num(q).astype(np.int32)  # an integer code: no signed zero
-            ref = (q.astype(np.float32) * step_).astype(np.float16).view(np.uint16)
-        got = y[l, kv, h].cpu().numpy().view(np.uint16)
+            r32 = torch.from_numpy(q.astype(np.float32) * step_)
+            ref = r32.to(x.dtype).view(torch.int16).numpy().view(np.uint16)
+        got = y[l, kv, h].cpu().view(torch.int16).numpy().view(np.uint16)
         bad += int(np.count_nonzero(got != ref))
     assert bad == 0, "decoded values differ from the reference reconstruction"
 
@@ -188,11 +209,12 @@ def main():
     n_tables = 2 * lv.n_groups * cfg.kv_heads * cfg.head_dim
     dec_tables = n_tables * 2048
     phases = {
-        "k_hist": (kms["build"], fp16_bytes + fmt),
+        "k_hist": (kms["build"], 2 * x_tab.numel() + fmt),
         "k_encode": (kms["encode"], fp16_bytes + comp),
         "k_decode": (kms["decode"], fp16_bytes + comp + dec_tables),
     }
     dom = max(phases, key=lambda k: phases[k][0])
+    variant = args.config + ("-bf16" if bf else "") + ("-robust" if args.robust else "")
 
     def roof(name):
         t, b = phases[name]
@@ -200,10 +222,10 @@ def main():
         r = {"kernel": name, "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
              "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
              "algorithmic_bytes": int(b), "avg_ms": round(float(t), 4)}
-        # counters taken on these very kernel sources only
+        # counters taken on these very kernel sources and this workload only
         try:
             with open(args.traffic) as f:
-                tr = json.load(f).get(args.config, {})
+                tr = json.load(f).get(variant, {})
             ent = tr.get("kernels", {}).get(name)
             if ent and tr.get("source_hash") == profiling.source_hash():
                 r["traffic"] = ent["bytes_per_launch"]
@@ -217,7 +239,7 @@ def main():
         int32 / non-packed fp32 VALU peak of 256 CUs x 64 lanes x 2.4 GHz."""
         try:
             with open(args.traffic) as f:
-                tr = json.load(f).get(args.config, {})
+                tr = json.load(f).get(variant, {})
             ent = tr.get("sq", {}).get(name)
             if not ent or tr.get("source_hash") != profiling.source_hash():
                 return None
@@ -240,12 +262,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16 data; fp32 quantize/dequantize, u32 rANS",
+        "dtype": "%s data; fp32 quantize/dequantize, u32 rANS" % args.dtype,
         "data": "synthetic",
-        "config": {"workload": "%s: %d layers x %d KV heads x %d dim x %d tokens, fp16 K+V, chunk %d, "
-                               "%s steps %s" % (cfg.name, cfg.layers, cfg.kv_heads, cfg.head_dim,
-                                                cfg.tokens, cfg.chunk_tokens, lvd.name,
-                                                "/".join(str(s) for s in lvd.steps)),
+        "config": {"workload": "%s: %d layers x %d KV heads x %d dim x %d tokens, %s K+V, chunk %d, "
+                               "%s steps %s%s" % (cfg.name, cfg.layers, cfg.kv_heads, cfg.head_dim,
+                                                  cfg.tokens, args.dtype, cfg.chunk_tokens, lvd.name,
+                                                  "/".join(str(s) for s in lvd.steps),
+                                                  ", robust tables from the first %d tokens" % (cfg.tokens // 4)
+                                                  if args.robust else ""),
                    "fp16_bytes": fp16_bytes, "chunks": nch},
         "decode_GBps": round(fp16_bytes / (t_dec / 1e3) / 1e9, 1),
         "encode_GBps": round(fp16_bytes / (t_enc / 1e3) / 1e9, 1),
@@ -268,7 +292,8 @@ def main():
         if copy_gbps else None,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, X, args.cpu_seconds)
+        xb = x[:1].cpu().view(torch.int16).numpy().view(np.uint16)
+        res["cpu_baseline"] = cpu_baseline(cfg, xb, args.cpu_seconds, dt, flags)
     print(json.dumps(res), flush=True)
 
 

@@ -102,7 +102,8 @@ __device__ __forceinline__ float cvt_f32_sext16(int32_t v) {
 // q = clamp(rint_even(fl32(x / step)), -32768, 32767), NaN -> 0.
 // FAST: v1 = x*r, e = x - v1*step (exact by FMA), v = v1 + e*r with r = RN(1/step);
 // used only for steps where k_qcheck proved it equal to the IEEE quotient for
-// every fp16 input. Branch-free; sat / nan_ count saturated and NaN inputs.
+// every input of the element type. Branch-free; sat / nan_ count saturated and
+// NaN inputs.
 template <bool FAST, bool BF>
 __device__ __forceinline__ int32_t quantize(uint16_t xh, float step, float rcp, uint32_t& sat,
                                             uint32_t& nan_) {
@@ -112,7 +113,10 @@ __device__ __forceinline__ int32_t quantize(uint16_t xh, float step, float rcp, 
     const float v1 = x * rcp;
     const float e = __builtin_fmaf(-v1, step, x);
     const float v2 = __builtin_fmaf(e, rcp, v1);
-    v = (e == e) ? v2 : v1;  // non-finite x: keep x*r (Inf or NaN)
+    // v2 is NaN when x*r is not finite: x is Inf or NaN, or a finite x
+    // (bfloat16 reaches 3.4e38) overflows x*r; keep x*r, which saturates
+    // or gives NaN -> 0 as the quotient would
+    v = (v2 == v2) ? v2 : v1;
   } else {
     v = x / step;
   }
