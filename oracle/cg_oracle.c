@@ -891,3 +891,58 @@ int cgo_decode_chunk_paged(const cgo_shape* s, const uint8_t* blob, const uint8_
   if (!pool || !block_table || num_blocks <= 0) return CGO_ERR_INVALID_ARG;
   return decode_chunk_impl(s, blob, rec, rec_bytes, NULL, pool, num_blocks, block_table);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Attention over the restored cache. [P2] section 2.3: the decoded KV is    */
+/* filled into the model's cache and used by the model unchanged; [P3]      */
+/* 「vLLM中的PagedAttention优化」: attention reads K/V from physical blocks  */
+/* through a block table. READING: one new token per layer ("decode step"), */
+/* q_heads query heads sharing the kv_heads (query head qh uses kv head      */
+/* qh / (q_heads / kv_heads)), scores scale * q . k over the first n_tokens */
+/* tokens, softmax, weighted sum of V; all in binary64.                      */
+/*   q   element bits [layers][q_heads][head_dim]                           */
+/*   o   binary64 [layers][q_heads][head_dim]                               */
+/* ------------------------------------------------------------------------ */
+int cgo_attend_paged(const cgo_shape* s, int32_t q_heads, const uint16_t* q, const uint16_t* pool,
+                     int64_t num_blocks, const int32_t* bt, int64_t n_tokens, double scale,
+                     double* o) {
+  if (!shape_ok(s) || q_heads < s->kv_heads || q_heads % s->kv_heads != 0 || n_tokens < 1 ||
+      num_blocks < 1)
+    return CGO_ERR_INVALID_ARG;
+  int H = s->kv_heads, D = s->head_dim, G = q_heads / s->kv_heads;
+  for (int64_t t = 0; t < n_tokens; t += 16)
+    if (bt[t / 16] < 0 || bt[t / 16] >= num_blocks) return CGO_ERR_INVALID_ARG;
+  double* sc = (double*)malloc(sizeof(double) * (size_t)n_tokens);
+  double* qf = (double*)malloc(sizeof(double) * (size_t)D);
+  for (int l = 0; l < s->layers; l++)
+    for (int qh = 0; qh < q_heads; qh++) {
+      int h = qh / G;
+      for (int d = 0; d < D; d++)
+        qf[d] = elem_to_float(s->dtype, q[((size_t)l * q_heads + qh) * D + d]);
+      double m = -INFINITY;
+      for (int64_t t = 0; t < n_tokens; t++) {
+        size_t kb = ((((size_t)l * 2 + 0) * (size_t)num_blocks + (size_t)bt[t / 16]) * H + h) * 16 +
+                    (size_t)(t % 16);
+        double acc = 0.0;
+        for (int d = 0; d < D; d++) acc += qf[d] * (double)elem_to_float(s->dtype, pool[kb * D + d]);
+        sc[t] = scale * acc;
+        if (sc[t] > m) m = sc[t];
+      }
+      double den = 0.0;
+      for (int64_t t = 0; t < n_tokens; t++) {
+        sc[t] = exp(sc[t] - m);
+        den += sc[t];
+      }
+      double* out = o + ((size_t)l * q_heads + qh) * D;
+      for (int d = 0; d < D; d++) out[d] = 0.0;
+      for (int64_t t = 0; t < n_tokens; t++) {
+        size_t vb = ((((size_t)l * 2 + 1) * (size_t)num_blocks + (size_t)bt[t / 16]) * H + h) * 16 +
+                    (size_t)(t % 16);
+        for (int d = 0; d < D; d++) out[d] += sc[t] * (double)elem_to_float(s->dtype, pool[vb * D + d]);
+      }
+      for (int d = 0; d < D; d++) out[d] /= den;
+    }
+  free(sc);
+  free(qf);
+  return CGO_OK;
+}

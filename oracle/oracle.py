@@ -99,6 +99,8 @@ def lib():
         L.cgo_decode_chunk.restype = ctypes.c_int
         L.cgo_decode_chunk_paged.argtypes = [sp, P, P, u64, P, i64, P]
         L.cgo_decode_chunk_paged.restype = ctypes.c_int
+        L.cgo_attend_paged.argtypes = [sp, i32, P, P, i64, P, i64, ctypes.c_double, P]
+        L.cgo_attend_paged.restype = ctypes.c_int
         L.cgo_half_to_float_array.argtypes = [P, i64, P]
         L.cgo_float_to_half_array.argtypes = [P, i64, P]
         L.cgo_quantize_array.argtypes = [P, i64, ctypes.c_float, P]
@@ -348,3 +350,20 @@ def decode_all(shp: Shape, blob, data, offs, Y=None):
         if rc != OK:
             raise RuntimeError("cgo_decode_chunk failed on chunk %d: %d" % (c, rc))
     return Y
+
+
+# ---- attention over the restored (paged) cache ------------------------------
+def attend_paged(shp: Shape, q_bits: np.ndarray, pool: np.ndarray, block_table: np.ndarray,
+                 n_tokens: int, scale: float) -> np.ndarray:
+    """q_bits: element bits [L][Hq][D]; pool [L][2][NB][H][16][D] element bits.
+    Returns binary64 o [L][Hq][D]."""
+    q = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    pl = np.ascontiguousarray(pool).view(np.uint16)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    L, Hq, D = q.shape
+    o = np.zeros((L, Hq, D), dtype=np.float64)
+    rc = lib().cgo_attend_paged(ctypes.byref(shp), Hq, _p(q), _p(pl), pl.shape[2], _p(bt), int(n_tokens),
+                                float(scale), _p(o))
+    if rc != OK:
+        raise RuntimeError("cgo_attend_paged failed: %d" % rc)
+    return o
