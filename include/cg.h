@@ -252,6 +252,32 @@ cg_status cg_recency_levels(int64_t n_chunks, int64_t near_chunks, int64_t far_c
 
 /* ---- measurement helper ---------------------------------------------------- */
 
+/* ---- attention over the restored cache -------------------------------- */
+
+/* The consumer of the decoded cache ("CacheGen实战" 2.3: the decoded KV is
+ * filled into the model's cache and used unchanged; "vLLM中的PagedAttention
+ * 优化": K and V read from 16-token physical blocks through a block table).
+ * One new token per layer: for every layer l and query head qh (which reads
+ * kv head qh / (q_heads / kv_heads)),
+ *   o[l][qh][:] = sum_t softmax_t(scale * q[l][qh] . K[l][t]) V[l][t],  t < n_tokens,
+ * with K[l][t] = pool[l][0][bt[t/16]][h][t%16][:], V likewise from pool[l][1].
+ *   q_dev    elements of shape->dtype, [layers][q_heads][head_dim], 16-byte aligned
+ *   pool_dev [layers][2][num_blocks][kv_heads][16][head_dim] (as cg_decode_paged), 16-byte aligned
+ *   o_dev    fp32 [layers][q_heads][head_dim]
+ *   ws_dev   cg_attend_workspace_bytes (per-wavefront partial results), 256-byte aligned
+ * Limits: q_heads a multiple of kv_heads, at most 16 query heads per kv head
+ * (CG_ERR_UNSUPPORTED otherwise), head_dim 64, 128 or 256, n_tokens >= 1.
+ * Scores take fp32 sums of exact 16-bit products (matrix cores), the softmax
+ * and the weighted sum of V are fp32; the result agrees with the exact value
+ * to within a bound stated with the tests. A block-table entry outside
+ * [0, num_blocks) writes CG_ERR_INVALID_ARG to *status_dev (its page is
+ * skipped). prof (optional) brackets the main kernel (k_attend). */
+size_t cg_attend_workspace_bytes(const cg_shape* shape, int32_t q_heads, int64_t n_tokens);
+cg_status cg_attend_paged(const cg_shape* shape, int32_t q_heads, const uint16_t* q_dev,
+                          const uint16_t* pool_dev, int64_t num_blocks, const int32_t* block_table_dev,
+                          int64_t n_tokens, float scale, float* o_dev, void* ws_dev, size_t ws_bytes,
+                          int32_t* status_dev, const cg_profile* prof, hipStream_t stream);
+
 /* Plain device copy of `bytes` (a multiple of 16) with the library's launch
  * style; used to calibrate achievable bandwidth and HBM counters. */
 cg_status cg_copy(void* dst_dev, const void* src_dev, uint64_t bytes, hipStream_t stream);

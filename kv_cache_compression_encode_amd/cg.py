@@ -142,6 +142,8 @@ def lib():
         "cg_select_level": (i32, [ctypes.c_double]),
         "cg_recency_levels": (i32, [i64, i64, i64, P]),
         "cg_stream_decode_paged": (i32, [sp, i32, lp, P, P, P, P, i32, P, u64, P, P, i64, P, P, P, P]),
+        "cg_attend_workspace_bytes": (sz, [sp, i32, i64]),
+        "cg_attend_paged": (i32, [sp, i32, P, P, i64, P, i64, ctypes.c_float, P, P, sz, P, pp, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(L, name)
@@ -155,7 +157,7 @@ EXPORTS = ("cg_version", "cg_status_string", "cg_tables_bytes", "cg_tables_forma
            "cg_build_workspace_bytes", "cg_build_tables", "cg_encode_bound",
            "cg_encode_workspace_bytes", "cg_encode", "cg_make_refs", "cg_decode",
            "cg_decode_paged", "cg_stream_decode_paged", "cg_copy", "cg_select_level",
-           "cg_recency_levels")
+           "cg_recency_levels", "cg_attend_workspace_bytes", "cg_attend_paged")
 
 
 def status_string(code: int) -> str:
@@ -257,6 +259,18 @@ def cg_decode_paged(shp, levels, tables, refs, n_refs, pool, num_blocks, block_t
                                _ptr(pool), int(num_blocks), _ptr(block_table), _ptr(status),
                                _prof(prof), _stream(stream))
     _check("cg_decode_paged", rc)
+
+
+def cg_attend_workspace_bytes(shp, q_heads, n_tokens) -> int:
+    return lib().cg_attend_workspace_bytes(ctypes.byref(shp), int(q_heads), int(n_tokens))
+
+
+def cg_attend_paged(shp, q_heads, q, pool, num_blocks, block_table, n_tokens, scale, o, ws, status,
+                    prof=None, stream=None):
+    rc = lib().cg_attend_paged(ctypes.byref(shp), int(q_heads), _ptr(q), _ptr(pool), int(num_blocks),
+                               _ptr(block_table), int(n_tokens), float(scale), _ptr(o), _ptr(ws),
+                               ws.numel() * ws.element_size(), _ptr(status), _prof(prof), _stream(stream))
+    _check("cg_attend_paged", rc)
 
 
 def cg_stream_decode_paged(shp, levels, tables, records_host, offsets_host, table_of_record, n_records,

@@ -109,6 +109,17 @@ class Codec:
         C.cg_decode(self.shp, levels, tables, refs, n_refs, y, self.status, prof)
         return y
 
+    def attend_paged(self, q, pool, block_table, n_tokens, scale, o=None, prof=None):
+        """Attention of one new token per layer over the paged cache:
+        q [layers][q_heads][head_dim] of the shape's element type -> fp32 o."""
+        L, Hq, D = q.shape
+        if o is None:
+            o = torch.empty((L, Hq, D), dtype=torch.float32, device=self.device)
+        ws = self._workspace("attend", C.cg_attend_workspace_bytes(self.shp, Hq, n_tokens))
+        C.cg_attend_paged(self.shp, Hq, q, pool, pool.shape[2], block_table, n_tokens, scale, o, ws,
+                          self.status, prof)
+        return o
+
     def decode_paged(self, levels, tables, refs, n_refs, pool, block_table, prof=None):
         C.cg_decode_paged(self.shp, levels, tables, refs, n_refs, pool, pool.shape[2], block_table,
                           self.status, prof)

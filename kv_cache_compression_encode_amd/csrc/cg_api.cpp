@@ -514,6 +514,71 @@ cg_status cg_decode_paged(const cg_shape* shape, int32_t n_levels, const cg_leve
   return hip_status(e);
 }
 
+// Attention: pages per wavefront so that about 16K wavefronts share the
+// work (at least 4, at most 64 pages each: one block-table entry per lane).
+static int32_t attend_pages_per_wave(const Shape& s, int64_t n_pages) {
+  const int64_t total = (int64_t)s.L * s.H * n_pages;
+  const int64_t ppw = (total + 16383) / 16384;
+  return (int32_t)std::min<int64_t>(64, std::max<int64_t>(4, ppw));
+}
+
+static cg_status attend_args(const cg_shape* shape, int32_t q_heads, int64_t n_tokens, AttendArgs* a) {
+  Shape s;
+  cg_status rc = check_shape(shape, &s);
+  if (rc != CG_OK) return rc;
+  if (q_heads < s.H || q_heads % s.H != 0 || n_tokens < 1 || n_tokens >= (1ll << 40))
+    return CG_ERR_INVALID_ARG;
+  if (q_heads / s.H > 16 || (s.D != 64 && s.D != 128 && s.D != 256) || (int64_t)q_heads * s.L >= (1ll << 31))
+    return CG_ERR_UNSUPPORTED;
+  std::memset(a, 0, sizeof(*a));
+  a->s = s;
+  a->q_heads = q_heads;
+  a->G = q_heads / s.H;
+  a->n_tokens = n_tokens;
+  a->n_pages = (n_tokens + 15) / 16;
+  a->pages_per_wave = attend_pages_per_wave(s, a->n_pages);
+  a->n_parts = (a->n_pages + a->pages_per_wave - 1) / a->pages_per_wave;
+  return CG_OK;
+}
+
+size_t cg_attend_workspace_bytes(const cg_shape* shape, int32_t q_heads, int64_t n_tokens) {
+  AttendArgs a;
+  if (attend_args(shape, q_heads, n_tokens, &a) != CG_OK) return 0;
+  const uint64_t slots = (uint64_t)a.s.L * a.s.H * a.n_parts * a.G;
+  return (size_t)(align_up(slots * 2 * 4, 256) + align_up(slots * a.s.D * 4, 256));
+}
+
+cg_status cg_attend_paged(const cg_shape* shape, int32_t q_heads, const uint16_t* q_dev,
+                          const uint16_t* pool_dev, int64_t num_blocks, const int32_t* block_table_dev,
+                          int64_t n_tokens, float scale, float* o_dev, void* ws_dev, size_t ws_bytes,
+                          int32_t* status_dev, const cg_profile* prof, hipStream_t stream) {
+  AttendArgs a;
+  cg_status rc = attend_args(shape, q_heads, n_tokens, &a);
+  if (rc != CG_OK) return rc;
+  if (!q_dev || !aligned(q_dev, 16) || !pool_dev || !aligned(pool_dev, 16) || num_blocks < 1 ||
+      num_blocks >= (1ll << 31) || !block_table_dev || !aligned(block_table_dev, 4) || !o_dev ||
+      !aligned(o_dev, 4) || !ws_dev || !aligned(ws_dev, 256) || !status_dev || !aligned(status_dev, 4) ||
+      !(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+    return CG_ERR_INVALID_ARG;
+  if (ws_bytes < cg_attend_workspace_bytes(shape, q_heads, n_tokens)) return CG_ERR_INVALID_ARG;
+  const uint64_t slots = (uint64_t)a.s.L * a.s.H * a.n_parts * a.G;
+  a.q = q_dev;
+  a.pool = pool_dev;
+  a.num_blocks = num_blocks;
+  a.bt = block_table_dev;
+  a.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  a.part_ml = static_cast<float*>(ws_dev);
+  a.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(ws_dev) + align_up(slots * 2 * 4, 256));
+  a.o = o_dev;
+  a.status = status_dev;
+  hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(status_dev), 0, 1, stream);
+  if (e == hipSuccess) e = mark(prof, true, stream);
+  if (e == hipSuccess) e = launch_attend(a, stream);
+  if (e == hipSuccess) e = mark(prof, false, stream);
+  if (e == hipSuccess) e = launch_attend_reduce(a, stream);
+  return hip_status(e);
+}
+
 cg_status cg_stream_decode_paged(const cg_shape* shape, int32_t n_levels, const cg_level* levels,
                                  const void* const* tables_dev, const uint8_t* records_host,
                                  const uint64_t* offsets_host, const int32_t* table_of_record_host,

@@ -1658,6 +1658,238 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// attention of one new token per layer over the paged cache: the consumer
+// of the restored KV ("CacheGen实战" 2.3: the decoded cache is used by the
+// model unchanged; "vLLM中的PagedAttention优化": K/V in 16-token physical
+// blocks found through a block table). Query head qh reads kv head qh / G.
+//
+// k_attend: a wavefront takes pages_per_wave consecutive pages of one
+// (layer, kv head) and all G <= 16 query heads of that kv head:
+//   S = K_page (16 tokens x D) . Q^T (D x 16 head slots) on the matrix
+//       cores (v_mfma_f32_16x16x16 f16/bf16, fp32 accumulation; products of
+//       two 16-bit elements are exact in fp32);
+//   online softmax per head in base 2 (scores pre-scaled by scale*log2 e);
+//   O[g][d] += P[t][g] V[t][d] on the vector ALUs in fp32, each lane owning
+//       D/64 adjacent dims, P broadcast from LDS.
+// It writes its partial (running max, sum, unnormalised O) per head;
+// k_attend_reduce merges the partials of a (layer, query head).
+//
+// MFMA 16x16x16 operand layout (lane i, 4 elements j): A[i%16][4(i/16)+j],
+// B[4(i/16)+j][i%16], D[4(i/16)+j][i%16]. The contraction index is free to
+// permute as long as A and B agree: k-step 2c+h of lane group i/16 takes
+// dims 32c + 8(i/16) + 4h + j, so one 16-byte load per lane gives two steps.
+// ---------------------------------------------------------------------------
+constexpr int kAttWaves = 4;
+
+typedef _Float16 att_h4 __attribute__((ext_vector_type(4)));
+typedef short att_s4 __attribute__((ext_vector_type(4)));
+typedef float att_f4 __attribute__((ext_vector_type(4)));
+
+template <bool BF>
+__device__ __forceinline__ att_f4 mfma16(uint2 a, uint2 b, att_f4 c) {
+  if constexpr (BF)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(att_s4, a), __builtin_bit_cast(att_s4, b),
+                                                     c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(att_h4, a), __builtin_bit_cast(att_h4, b), c,
+                                                 0, 0, 0);
+}
+
+// ND = D / 64 dims per lane in the P.V product (D = 64, 128 or 256); GM =
+// head slots carried through P.V (4, 8 or 16 >= G; slots >= G see q = 0 and
+// are not written)
+template <bool BF, int ND, int GM>
+__global__ void __launch_bounds__(kAttWaves * 64) k_attend(AttendArgs a) {
+  constexpr int D = 64 * ND, KS = D / 32;  // 16-byte loads per lane per page
+  __shared__ float p_lds[kAttWaves][16][16];  // [token][head slot]
+  __shared__ float al_lds[kAttWaves][16];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int gi = lane & 15, gq = lane >> 4;
+  const int h = blockIdx.y, l = blockIdx.z;
+  const int64_t part = (int64_t)blockIdx.x * kAttWaves + wave;
+  if (part >= a.n_parts) return;
+  const Shape s = a.s;
+  const int G = a.G;
+  const int64_t pg0 = part * a.pages_per_wave;
+  const int64_t pg1 = pg0 + a.pages_per_wave < a.n_pages ? pg0 + a.pages_per_wave : a.n_pages;
+
+  // Q as the B operand: slot gi < G is query head h*G + gi, other slots 0
+  uint2 qb[KS][2];
+  {
+    const uint16_t* qrow = a.q + ((size_t)l * a.q_heads + (size_t)h * G + (gi < G ? gi : 0)) * D;
+#pragma unroll
+    for (int c = 0; c < KS; ++c) {
+      uint4 v = gi < G ? *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * gq) : make_uint4(0, 0, 0, 0);
+      qb[c][0] = make_uint2(v.x, v.y);
+      qb[c][1] = make_uint2(v.z, v.w);
+    }
+  }
+  const size_t kv_stride = (size_t)a.num_blocks * s.H * 16 * D;  // K -> V of a layer
+  const uint16_t* kbase = a.pool + (size_t)l * 2 * kv_stride + (size_t)h * 16 * D;
+  float m = -__builtin_inff();  // running max of head slot gi (log2 units)
+  float lsum = 0.0f;            // this lane's share of the running sum
+  float acc_o[GM][ND];
+#pragma unroll
+  for (int g = 0; g < GM; ++g)
+#pragma unroll
+    for (int k = 0; k < ND; ++k) acc_o[g][k] = 0.0f;
+
+  // block-table entries of this wavefront's pages, one per lane
+  // (pages_per_wave <= 64); an entry out of range is reported and its page
+  // skipped (its loads use block 0 so they stay in bounds)
+  const int npw = (int)(pg1 - pg0);
+  const int32_t bt_lane = lane < npw ? a.bt[pg0 + lane] : 0;
+  const bool bt_bad = lane < npw && (bt_lane < 0 || (int64_t)bt_lane >= a.num_blocks);
+  const uint64_t bad_pages = __ballot(bt_bad);
+  if (bad_pages && lane == 0) set_status(a.status, CG_ERR_INVALID_ARG);
+  const int32_t bt_safe = bt_bad ? 0 : bt_lane;
+
+  // one page in registers: K as MFMA A operands, V rows as this lane's dims
+  using VT = typename std::conditional<ND == 1, uint16_t, typename std::conditional<ND == 2, uint32_t, uint2>::type>::type;
+  auto load_page = [&](int i, uint4* kv, VT* vv) {
+    const int32_t blk = __builtin_amdgcn_readlane(bt_safe, i);
+    const uint16_t* kp = kbase + (size_t)blk * s.H * 16 * D;
+    const uint16_t* vp = kp + kv_stride;
+#pragma unroll
+    for (int c = 0; c < KS; ++c) kv[c] = *reinterpret_cast<const uint4*>(kp + gi * D + 32 * c + 8 * gq);
+    const int64_t left = a.n_tokens - (pg0 + i) * 16;
+    const int last = left < 16 ? (int)left - 1 : 15;  // rows past the end re-read the last valid one
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      vv[t] = *reinterpret_cast<const VT*>(vp + (t < last ? t : last) * D + ND * lane);
+  };
+  uint4 kc[KS], kn[KS];
+  VT vc[16], vn[16];
+  if (npw > 0) load_page(0, kc, vc);
+  // the first page lands before the loop, so that the loop's wait counts
+  // only cover the page being prefetched (see hist_range)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  for (int i = 0; i < npw; ++i) {
+    if (i + 1 < npw) load_page(i + 1, kn, vn);
+    const int64_t pg = pg0 + i;
+    if (!((bad_pages >> i) & 1)) {
+      const int64_t left = a.n_tokens - pg * 16;
+      const int nv = left < 16 ? (int)left : 16;  // valid tokens of this page
+      // S = K Q^T
+      att_f4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < KS; ++c) {
+        sc = mfma16<BF>(make_uint2(kc[c].x, kc[c].y), qb[c][0], sc);
+        sc = mfma16<BF>(make_uint2(kc[c].z, kc[c].w), qb[c][1], sc);
+      }
+      // sc[j] = S[token 4 gq + j][slot gi]; tokens past the end do not count
+      float sv[4];
+      float pm = -__builtin_inff();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sv[j] = 4 * gq + j < nv ? sc[j] * a.scale_log2e : -__builtin_inff();
+        pm = __builtin_fmaxf(pm, sv[j]);
+      }
+      pm = __builtin_fmaxf(pm, __shfl_xor(pm, 16));
+      pm = __builtin_fmaxf(pm, __shfl_xor(pm, 32));
+      const float m_new = __builtin_fmaxf(m, pm);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first page
+      float ps = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float pj = __builtin_amdgcn_exp2f(sv[j] - m_new);
+        p_lds[wave][4 * gq + j][gi] = pj;
+        ps += pj;
+      }
+      lsum = lsum * alpha + ps;
+      m = m_new;
+      if (gq == 0) al_lds[wave][gi] = alpha;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // O = diag(alpha) O + P^T V (rows past the end have P = 0)
+      {
+        float al[GM];
+#pragma unroll
+        for (int g4 = 0; g4 < GM / 4; ++g4)
+          *reinterpret_cast<float4*>(&al[4 * g4]) = *reinterpret_cast<const float4*>(&al_lds[wave][4 * g4]);
+#pragma unroll
+        for (int g = 0; g < GM; ++g)
+#pragma unroll
+          for (int k = 0; k < ND; ++k) acc_o[g][k] *= al[g];
+      }
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        float v[ND];
+        if constexpr (ND == 1) {
+          v[0] = elem_to_f32<BF>(vc[t]);
+        } else if constexpr (ND == 2) {
+          v[0] = elem_to_f32<BF>((uint16_t)vc[t]);
+          v[1] = elem_to_f32<BF>((uint16_t)(vc[t] >> 16));
+        } else {
+          v[0] = elem_to_f32<BF>((uint16_t)vc[t].x);
+          v[1] = elem_to_f32<BF>((uint16_t)(vc[t].x >> 16));
+          v[2] = elem_to_f32<BF>((uint16_t)vc[t].y);
+          v[3] = elem_to_f32<BF>((uint16_t)(vc[t].y >> 16));
+        }
+        float pt[GM];
+#pragma unroll
+        for (int g4 = 0; g4 < GM / 4; ++g4)
+          *reinterpret_cast<float4*>(&pt[4 * g4]) = *reinterpret_cast<const float4*>(&p_lds[wave][t][4 * g4]);
+#pragma unroll
+        for (int g = 0; g < GM; ++g)
+#pragma unroll
+          for (int k = 0; k < ND; ++k) acc_o[g][k] = __builtin_fmaf(pt[g], v[k], acc_o[g][k]);
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+#pragma unroll
+    for (int c = 0; c < KS; ++c) kc[c] = kn[c];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) vc[t] = vn[t];
+  }
+  // partial of this wavefront: max and sum per head slot, unnormalised O
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  const size_t pbase = (((size_t)l * s.H + h) * a.n_parts + part) * G;
+  if (gq == 0 && gi < G) {
+    a.part_ml[2 * (pbase + gi)] = m;
+    a.part_ml[2 * (pbase + gi) + 1] = lsum;
+  }
+#pragma unroll
+  for (int g = 0; g < GM; ++g) {
+    if (g < G) {
+      float* po = a.part_o + (pbase + g) * D + ND * lane;
+#pragma unroll
+      for (int k = 0; k < ND; ++k) po[k] = acc_o[g][k];
+    }
+  }
+}
+
+// One wavefront per (layer, query head): merge the partials.
+template <int ND>
+__global__ void __launch_bounds__(64) k_attend_reduce(AttendArgs a) {
+  constexpr int D = 64 * ND;
+  const int lane = threadIdx.x;
+  const int qh = blockIdx.x, l = blockIdx.y;
+  const int h = qh / a.G, g = qh % a.G;
+  const size_t base = ((size_t)l * a.s.H + h) * a.n_parts * a.G + g;  // + part * G
+  float M = -__builtin_inff();
+  for (int64_t p = 0; p < a.n_parts; ++p) M = __builtin_fmaxf(M, a.part_ml[2 * (base + p * a.G)]);
+  float den = 0.0f, o[ND];
+#pragma unroll
+  for (int k = 0; k < ND; ++k) o[k] = 0.0f;
+  for (int64_t p = 0; p < a.n_parts; ++p) {
+    const size_t i = base + p * a.G;
+    const float w = __builtin_amdgcn_exp2f(a.part_ml[2 * i] - M);
+    den = __builtin_fmaf(w, a.part_ml[2 * i + 1], den);
+    const float* po = a.part_o + i * D + ND * lane;
+#pragma unroll
+    for (int k = 0; k < ND; ++k) o[k] = __builtin_fmaf(w, po[k], o[k]);
+  }
+  float* out = a.o + ((size_t)l * a.q_heads + qh) * D + ND * lane;
+#pragma unroll
+  for (int k = 0; k < ND; ++k) out[k] = o[k] / den;
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 static unsigned grid_for(uint64_t n, unsigned threads, unsigned cap) {
@@ -1745,6 +1977,43 @@ hipError_t launch_chunk_scan(const ChunkScanArgs& a, hipStream_t st) {
 hipError_t launch_write(const WriteArgs& a, hipStream_t st) {
   const int64_t nblk = 1 + (a.gpc + a.groups_per_block - 1) / a.groups_per_block;
   hipLaunchKernelGGL(k_write, dim3((unsigned)(a.n_chunks * nblk)), dim3(kWriteThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <bool BF, int ND>
+static void launch_attend_nd(const AttendArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)((a.n_parts + kAttWaves - 1) / kAttWaves), (unsigned)a.s.H, (unsigned)a.s.L);
+  if (a.G <= 4)
+    hipLaunchKernelGGL((k_attend<BF, ND, 4>), grid, dim3(kAttWaves * 64), 0, st, a);
+  else if (a.G <= 8)
+    hipLaunchKernelGGL((k_attend<BF, ND, 8>), grid, dim3(kAttWaves * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_attend<BF, ND, 16>), grid, dim3(kAttWaves * 64), 0, st, a);
+}
+
+template <bool BF>
+static hipError_t launch_attend_t(const AttendArgs& a, hipStream_t st) {
+  switch (a.s.D) {
+    case 64: launch_attend_nd<BF, 1>(a, st); break;
+    case 128: launch_attend_nd<BF, 2>(a, st); break;
+    case 256: launch_attend_nd<BF, 4>(a, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
+  return a.s.dt == kDtypeBf16 ? launch_attend_t<true>(a, st) : launch_attend_t<false>(a, st);
+}
+
+hipError_t launch_attend_reduce(const AttendArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)a.q_heads, (unsigned)a.s.L);
+  switch (a.s.D) {
+    case 64: hipLaunchKernelGGL((k_attend_reduce<1>), grid, dim3(64), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((k_attend_reduce<2>), grid, dim3(64), 0, st, a); break;
+    case 256: hipLaunchKernelGGL((k_attend_reduce<4>), grid, dim3(64), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -188,6 +188,23 @@ struct WriteArgs {
   int groups_per_block;
 };
 
+struct AttendArgs {
+  Shape s;
+  int q_heads, G;              // G = q_heads / kv_heads <= 16
+  const uint16_t* q;           // [L][q_heads][D] element bits
+  const uint16_t* pool;        // [L][2][num_blocks][H][16][D]
+  int64_t num_blocks;
+  const int32_t* bt;           // [ceil(n_tokens / 16)]
+  int64_t n_tokens, n_pages;
+  int32_t pages_per_wave;
+  int64_t n_parts;             // partials per (layer, kv head)
+  float scale_log2e;           // softmax scale * log2(e)
+  float* part_ml;              // [L][H][n_parts][G][2]: running max (log2 units), sum
+  float* part_o;               // [L][H][n_parts][G][D]: unnormalised output
+  float* o;                    // [L][q_heads][D]
+  int32_t* status;
+};
+
 struct DecodeArgs {
   Shape s;
   const cg_chunk_ref* refs;
@@ -221,6 +238,8 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t st);
 hipError_t launch_chunk_scan(const ChunkScanArgs& a, hipStream_t st);
 hipError_t launch_write(const WriteArgs& a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, bool paged, hipStream_t st);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
+hipError_t launch_attend_reduce(const AttendArgs& a, hipStream_t st);
 hipError_t launch_make_refs(const uint8_t* base, const uint64_t* offs, int32_t n, int32_t table,
                             cg_chunk_ref* refs, hipStream_t st);
 hipError_t launch_copy(void* dst, const void* src, uint64_t bytes, hipStream_t st);

@@ -9,6 +9,8 @@ from kv_cache_compression_encode_amd import cg as C  # noqa: E402
 from kv_cache_compression_encode_amd import codec  # noqa: E402
 from oracle import oracle as O  # noqa: E402
 
+__all__ = ["C", "codec", "O", "torch"]
+
 
 def need_gpu():
     if not torch.cuda.is_available():
