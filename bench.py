@@ -13,7 +13,9 @@ the roofline of the dominant kernel and the CPU oracle timed on a sample.
 Variants (their own lines, not the headline): --dtype bf16 runs the same
 workload as bfloat16 elements (the fp16 draw rounded to bfloat16);
 --robust builds robust tables from the first quarter of the tokens only
-(calibration data) and encodes the whole cache with them.
+(calibration data) and encodes the whole cache with them; --attend times
+the restore-and-consume step instead: cg_decode_paged of every chunk into a
+paged pool, then cg_attend_paged of one new token per layer over it.
 """
 from __future__ import annotations
 
@@ -78,6 +80,8 @@ def main():
     ap.add_argument("--dtype", choices=("fp16", "bf16"), default="fp16")
     ap.add_argument("--robust", action="store_true",
                     help="robust tables from the first quarter of the tokens")
+    ap.add_argument("--attend", action="store_true",
+                    help="time decode into a paged pool + attention over it")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed steps, one library copy of this many bytes (the calibration "
                          "launch for the FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -143,6 +147,9 @@ def main():
         cd.decode([lv], [tables], refs, nch, y=y, prof=kt.get("decode"))
         if ev:
             ev[4].record(stream)
+
+    if args.attend:
+        return run_attend(args, cfg, lvd, cd, x, shp, lv, tables, out, offs, refs, nch, stream)
 
     for _ in range(args.warmup):
         step()
@@ -294,6 +301,128 @@ def main():
     if not args.no_cpu_baseline:
         xb = x[:1].cpu().view(torch.int16).numpy().view(np.uint16)
         res["cpu_baseline"] = cpu_baseline(cfg, xb, args.cpu_seconds, dt, flags)
+    print(json.dumps(res), flush=True)
+
+
+# query heads per kv head of the models the workloads are shaped after
+# (34B: 64 query heads over 8 kv heads; 7B: 32 over 32)
+Q_HEADS = {"tiny": 4, "7b": 32, "34b": 64, "long": 64, "stream": 32}
+
+
+def run_attend(args, cfg, lvd, cd, x, shp, lv, tables, out, offs, refs, nch, stream):
+    """Step = cg_decode_paged of every chunk into a paged pool (random block
+    placement) + cg_attend_paged of one new token per layer over the pool."""
+    import numpy as np
+    import torch
+
+    from kv_cache_compression_encode_amd import cg as C
+    from kv_cache_compression_encode_amd import profiling
+
+    dev = x.device
+    cd.build_tables(x, lv, tables=tables)
+    cd.encode(x, lv, tables, out=out, offsets=offs)
+    C.cg_make_refs(out, offs, nch, 0, refs)
+    torch.cuda.synchronize()
+    assert cd.read_status() == 0
+    nbl = -(-cfg.tokens // 16)
+    bt = torch.from_numpy(np.random.default_rng([0, cfg.config_id, 998]).permutation(nbl).astype(np.int32)).to(dev)
+    del x
+    from kv_cache_compression_encode_amd.codec import torch_dtype
+    pool = torch.empty((cfg.layers, 2, nbl, cfg.kv_heads, 16, cfg.head_dim), dtype=torch_dtype(shp), device=dev)
+    Hq = Q_HEADS[cfg.name]
+    g = torch.Generator(device="cpu").manual_seed(7)
+    q = torch.randn((cfg.layers, Hq, cfg.head_dim), generator=g).to(torch_dtype(shp)).to(dev)
+    o = torch.empty((cfg.layers, Hq, cfg.head_dim), dtype=torch.float32, device=dev)
+    scale = 1.0 / float(np.sqrt(cfg.head_dim))
+
+    def step(ev=None, kt=None):
+        kt = kt or {}
+        if ev:
+            ev[0].record(stream)
+        cd.decode_paged([lv], [tables], refs, nch, pool, bt, prof=kt.get("decode"))
+        if ev:
+            ev[1].record(stream)
+        cd.attend_paged(q, pool, bt, cfg.tokens, scale, o=o, prof=kt.get("attend"))
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert cd.read_status() == 0
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    timers = [{k: C.KernelTimer() for k in ("decode", "attend")} for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k], timers[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert cd.read_status() == 0
+    ms = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(2)] for e in events])
+    t_dec, t_att = ms.mean(axis=0)
+    kms = {k: float(np.mean([t[k].elapsed_ms() for t in timers])) for k in ("decode", "attend")}
+    kv_bytes = 2 * cfg.n_elements
+    comp = int(offs[-1].item())
+    ws = C.cg_attend_workspace_bytes(shp, Hq, cfg.tokens)
+    # k_attend reads K and V once, q once, and writes its partials
+    att_bytes = kv_bytes + q.numel() * 2 + ws
+    # correctness of this run: sampled (layer, query head) against the same
+    # definition in float64 on the host, within the bound the tests use
+    rng = np.random.default_rng(1)
+    G = Hq // cfg.kv_heads
+    tdt = torch_dtype(shp)
+    worst = 0.0
+    for _ in range(3):
+        l, qh = int(rng.integers(cfg.layers)), int(rng.integers(Hq))
+        h = qh // G
+        K = pool[l, 0][bt.long(), h].reshape(-1, cfg.head_dim).to(torch.float64).cpu().numpy()
+        V = pool[l, 1][bt.long(), h].reshape(-1, cfg.head_dim).to(torch.float64).cpu().numpy()
+        qv = q[l, qh].to(torch.float64).cpu().numpy()
+        sc = scale * (K @ qv)
+        p = np.exp(sc - sc.max())
+        ref = (p @ V) / p.sum()
+        tol = np.abs(V).max() * (4 * scale * cfg.head_dim * 2.0**-24 * np.abs(K * qv).sum(axis=1).max() + 1e-4)
+        err = float(np.abs(o[l, qh].cpu().numpy().astype(np.float64) - ref).max())
+        assert err <= tol, (l, qh, err, tol)
+        worst = max(worst, err / tol)
+    gbps = att_bytes / (kms["attend"] / 1e3) / 1e9
+    roof = {"kernel": "k_attend", "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+            "algorithmic_bytes": int(att_bytes), "avg_ms": round(kms["attend"], 4)}
+    variant = args.config + ("-bf16" if shp.dtype == C.CG_DTYPE_BF16 else "") + "-attend"
+    try:
+        with open(args.traffic) as f:
+            tr = json.load(f).get(variant, {})
+        ent = tr.get("kernels", {}).get("k_attend")
+        if ent and tr.get("source_hash") == profiling.source_hash():
+            roof["traffic"] = ent["bytes_per_launch"]
+    except (OSError, ValueError):
+        pass
+    res = {
+        "metric": METRIC,
+        "value": round(kv_bytes / (wall / args.steps) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "%s data; fp32 softmax and P.V, MFMA %s scores" % (args.dtype, args.dtype),
+        "data": "synthetic",
+        "config": {"workload": "%s restore + attend: decode %d chunk records into a paged pool (16-token "
+                               "blocks, random placement), then one new token per layer, %d query heads over "
+                               "%d kv heads x %d tokens" % (cfg.name, nch, Hq, cfg.kv_heads, cfg.tokens),
+                   "kv_bytes": kv_bytes, "compressed_bytes": comp},
+        "decode_paged_ms": round(float(t_dec), 4),
+        "attend_ms": round(float(t_att), 4),
+        "kernel_ms": {"k_decode_paged": round(kms["decode"], 4), "k_attend": round(kms["attend"], 4)},
+        "attend_GBps": round(gbps, 1),
+        "roofline": roof,
+        "attend_err_over_bound": round(worst, 4),
+    }
     print(json.dumps(res), flush=True)
 
 

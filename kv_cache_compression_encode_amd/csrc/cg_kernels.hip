@@ -1108,6 +1108,7 @@ struct Chain {
   int n;
   uint32_t bt0, bt1;           // paged: block-table entries of blocks bt_base + lane, + 64
   int64_t bt_base;
+  uint32_t pg_left;            // paged: tokens left in the current page after the last stored one
   bool ok;
   // values carried between the phases of one token (pipelined loop)
   uint32_t above, rankx, info, w;
@@ -1145,6 +1146,21 @@ __device__ __forceinline__ uint32_t row_offset(const DecodeArgs& a, Chain& c, in
   const uint32_t blk = bi < 64 ? (uint32_t)__builtin_amdgcn_readlane(c.bt0, bi)
                                : (uint32_t)__builtin_amdgcn_readlane(c.bt1, bi - 64);
   return ((blk * (uint32_t)a.s.H + (uint32_t)h) * 16u + (uint32_t)(t & 15)) * row_bytes;
+}
+
+// Output row of token i of the chain, from the previous one: the next row of
+// the same 16-token page, or at a page boundary the page the block table
+// names (contiguous output: always the next row).
+template <bool PAGED>
+__device__ __forceinline__ void next_row(const DecodeArgs& a, Chain& c, int i, int h, uint32_t row_bytes,
+                                         int lane) {
+  if (!PAGED || c.pg_left != 0) {
+    c.doff += row_bytes;
+    if (PAGED) c.pg_left -= 1;
+  } else {
+    c.doff = row_offset<PAGED>(a, c, c.t0 + i, h, row_bytes, lane);
+    c.pg_left = 15;
+  }
 }
 
 __device__ __forceinline__ void ring_put(Chain& c, uint32_t wbase, uint32_t v, int lane) {
@@ -1210,6 +1226,7 @@ __device__ __forceinline__ void chain_open(const DecodeArgs& a, Chain& c, const 
     c.bt1 = i1 <= last ? (uint32_t)a.block_table[i1] : 0u;
   }
   c.doff = row_offset<PAGED>(a, c, gr.t0, h, row_bytes, lane);
+  c.pg_left = 15u - (uint32_t)(gr.t0 & 15);
   __builtin_amdgcn_raw_buffer_store_b16(dequantize_low16<BF>(c.q, step), c.dst, 2u * lane, c.doff, 0);
 }
 
@@ -1301,7 +1318,7 @@ __device__ __forceinline__ void chain_steps(const DecodeArgs& a, Chain* c, int i
     for (int k = 0; k < NC; ++k) {
       const uint16_t y = dequantize_low16<BF>(c[k].q, step);
       if (PAGED)
-        c[k].doff = row_offset<PAGED>(a, c[k], c[k].t0 + i, h, row_bytes, lane);
+        next_row<PAGED>(a, c[k], i, h, row_bytes, lane);
       else
         c[k].doff += row_bytes;
       __builtin_amdgcn_raw_buffer_store_b16(y, c[k].dst, lane2, c[k].doff, 0);
@@ -1409,7 +1426,7 @@ __device__ __forceinline__ void ph_d(const DecodeArgs& a, Chain& c, int i, int h
   }
   const uint16_t y = dequantize_low16<BF>(c.q, step);
   if (PAGED)
-    c.doff = row_offset<PAGED>(a, c, c.t0 + i, h, row_bytes, lane);
+    next_row<PAGED>(a, c, i, h, row_bytes, lane);
   else
     c.doff += row_bytes;
   __builtin_amdgcn_raw_buffer_store_b16(y, c.dst, 2u * lane, c.doff, 0);

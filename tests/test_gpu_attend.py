@@ -139,3 +139,36 @@ def test_decode_then_attend(dtype):
     tol = bound(f64_of(q_bits, dtype), f64_of(opool, dtype), bt, T, scale, G)
     err = np.abs(got.cpu().numpy().astype(np.float64) - ref).max(axis=2)
     assert np.all(err <= tol), (err.max(), tol.min())
+
+
+def test_attend_full_size_sampled():
+    """The 34B shape (48 layers, 8 kv heads, 64 query heads, 128 dims, 32768
+    tokens, pages placed at random) in the launch configuration the bench
+    times; sampled (layer, query head) pairs against the oracle."""
+    U.need_gpu()
+    torch = U.torch
+    L, H, G, D, T = 48, 8, 8, 128, 32768
+    nbl = T // 16
+    gen = torch.Generator(device="cuda").manual_seed(44)
+    pool = torch.randn((L, 2, nbl, H, 16, D), generator=gen, device="cuda").to(torch.float16)
+    q = torch.randn((L, H * G, D), generator=gen, device="cuda").to(torch.float16)
+    bt = np.random.default_rng(45).permutation(nbl).astype(np.int32)
+    btd = torch.from_numpy(bt).cuda()
+    cd = U.codec.Codec(U.C.shape(L, H, D, T, 1536))
+    scale = 1.0 / np.sqrt(D)
+    o = cd.attend_paged(q, pool, btd, T, scale)
+    assert cd.read_status() == 0
+    rng = np.random.default_rng(46)
+    ident = np.arange(nbl, dtype=np.int32)
+    for _ in range(4):
+        l, qh = int(rng.integers(L)), int(rng.integers(H * G))
+        h = qh // G
+        sub = pool[l][:, btd.long(), h].unsqueeze(0).unsqueeze(3).contiguous()  # [1][2][nbl][1][16][D]
+        sub_bits = sub.cpu().view(torch.int16).numpy().view(np.uint16)
+        q_bits = q[l, qh].reshape(1, 1, D).cpu().view(torch.int16).numpy().view(np.uint16)
+        ref = U.O.attend_paged(U.O.shape(1, 1, D, T, 1536), q_bits, sub_bits, ident, T,
+                               float(np.float32(scale)))[0, 0]
+        tol = bound(f64_of(q_bits, F16), f64_of(sub_bits, F16), ident, T, scale, 1)[0, 0]
+        err = np.abs(o[l, qh].cpu().numpy().astype(np.float64) - ref).max()
+        print("sample", l, qh, "err", err, "bound", tol, flush=True)
+        assert err <= tol
