@@ -13,8 +13,9 @@
 // Kernels
 //   k_fill_u32     fill (no hipMemset, so calls stay capturable)
 //   k_blob_init    tables-blob header, steps, layer groups
-//   k_qcheck       per layer group: is the 4-flop quotient exact for all 65536
-//                  inputs of the element type? (else the IEEE divide is used)
+//   k_qcheck       per layer group: is x*(1/step), or failing that its one-FMA
+//                  correction, exact for all 65536 inputs of the element type?
+//                  (else the IEEE divide is used)
 //   k_hist         quantize + delta + symbol, LDS-privatised 64 x 256 counts
 //   k_norm         one wavefront per table: 12-bit normalisation, cumulative
 //                  frequencies, encoder / decoder lookup tables
@@ -100,16 +101,25 @@ __device__ __forceinline__ float cvt_f32_sext16(int32_t v) {
 }
 
 // q = clamp(rint_even(fl32(x / step)), -32768, 32767), NaN -> 0.
-// FAST: v1 = x*r, e = x - v1*step (exact by FMA), v = v1 + e*r with r = RN(1/step);
-// used only for steps where k_qcheck proved it equal to the IEEE quotient for
-// every input of the element type. Branch-free; sat / nan_ count saturated and
-// NaN inputs.
-template <bool FAST, bool BF>
+// Three ways to the quotient, QM:
+//   kQuotDiv   the IEEE binary32 divide;
+//   kQuotFma   v1 = x*r, e = x - v1*step (exact by FMA), v = v1 + e*r with
+//              r = RN(1/step);
+//   kQuotMul   v = x*r.
+// The two cheap ones are used only for steps where k_qcheck proved that they
+// give the same q as the divide for every input of the element type.
+// Branch-free; sat / nan_ count saturated and NaN inputs.
+constexpr int kQuotDiv = 0, kQuotFma = 1, kQuotMul = 2;
+
+template <int QM, bool BF>
 __device__ __forceinline__ int32_t quantize(uint16_t xh, float step, float rcp, uint32_t& sat,
                                             uint32_t& nan_) {
+  constexpr bool FAST = QM != kQuotDiv;
   const float x = elem_to_f32<BF>(xh);
   float v;
-  if (FAST) {
+  if (QM == kQuotMul) {
+    v = x * rcp;  // NaN stays NaN, Inf and overflow saturate below
+  } else if (QM == kQuotFma) {
     const float v1 = x * rcp;
     const float e = __builtin_fmaf(-v1, step, x);
     const float v2 = __builtin_fmaf(e, rcp, v1);
@@ -225,8 +235,11 @@ __device__ __forceinline__ bool blob_ok(const uint8_t* b, const Shape& s, int G)
          (int)uni(bh->H) == s.H && (int)uni(bh->D) == s.D && (int)uni(bh->G) == G &&
          (int)uni(bh->dtype) == s.dt && (uni(bh->flags) & ~kTablesRobust) == 0;
 }
-__device__ __forceinline__ bool qflag(const uint8_t* b, int L, int H, int D, int G, int g) {
-  return uni(reinterpret_cast<const uint32_t*>(b + tb_qflag_offset(L, H, D, G))[g]) != 0;
+// Quotient mode of layer group g: bit 0 of the flag = kQuotFma proven exact,
+// bit 1 = kQuotMul proven exact (k_qcheck clears what fails).
+__device__ __forceinline__ int qmode(const uint8_t* b, int L, int H, int D, int G, int g) {
+  const uint32_t f = uni(reinterpret_cast<const uint32_t*>(b + tb_qflag_offset(L, H, D, G))[g]);
+  return (f & 2u) ? kQuotMul : (f & 1u) ? kQuotFma : kQuotDiv;
 }
 
 // ---------------------------------------------------------------------------
@@ -306,7 +319,7 @@ __global__ void k_blob_init(BlobInitArgs a) {
     h[15] = 0;
   }
   uint32_t* qf = reinterpret_cast<uint32_t*>(b + tb_qflag_offset(a.L, a.H, a.D, a.G));
-  for (int g = threadIdx.x; g < 256; g += blockDim.x) qf[g] = g < a.G ? 1u : 0u;
+  for (int g = threadIdx.x; g < 256; g += blockDim.x) qf[g] = g < a.G ? 3u : 0u;
 }
 
 template <bool BF>
@@ -316,9 +329,11 @@ __global__ void k_qcheck(QCheckArgs a) {
   const float step = blob_step(a.blob, g);
   const float rcp = 1.0f / step;
   uint32_t s0 = 0, n0 = 0;
-  const int32_t qf = quantize<true, BF>((uint16_t)xh, step, rcp, s0, n0);
-  const int32_t qi = quantize<false, BF>((uint16_t)xh, step, rcp, s0, n0);
-  if (qf != qi) atomicAnd(&a.qflags[g], 0u);
+  const int32_t qi = quantize<kQuotDiv, BF>((uint16_t)xh, step, rcp, s0, n0);
+  const int32_t qf = quantize<kQuotFma, BF>((uint16_t)xh, step, rcp, s0, n0);
+  const int32_t qm = quantize<kQuotMul, BF>((uint16_t)xh, step, rcp, s0, n0);
+  if (qf != qi) atomicAnd(&a.qflags[g], ~1u);
+  if (qm != qi) atomicAnd(&a.qflags[g], ~2u);
 }
 
 // ---------------------------------------------------------------------------
@@ -336,7 +351,7 @@ constexpr int kHistBatch = 16;
 // Tokens [t_begin, t_end) of one (layer, K|V, head, slice) column; xr
 // covers the column from token 0 (row t at byte t * row_bytes). Every load
 // is in bounds by construction. STATS adds the saturated / NaN counts.
-template <bool FAST, bool STATS, bool BF>
+template <int QM, bool STATS, bool BF>
 __device__ __forceinline__ void hist_range(__amdgpu_buffer_rsrc_t xr, uint32_t row_bytes, int t_begin,
                                            int t_end, int C, float step, float rcp, uint32_t* hist,
                                            int lane, uint32_t& sat, uint32_t& nan_) {
@@ -346,13 +361,13 @@ __device__ __forceinline__ void hist_range(__amdgpu_buffer_rsrc_t xr, uint32_t r
   int pos = t_begin % C;  // position of the next token inside its chunk
   if (pos != 0) {
     uint32_t d0 = 0, d1 = 0;
-    prev = quantize<FAST, BF>(
+    prev = quantize<QM, BF>(
         (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, (uint32_t)(t_begin - 1) * row_bytes, 0),
         step, rcp, d0, d1);
   }
   auto one = [&](uint16_t xh) {
     uint32_t s0 = 0, n0 = 0;
-    const int32_t q = quantize<FAST, BF>(xh, step, rcp, s0, n0);
+    const int32_t q = quantize<QM, BF>(xh, step, rcp, s0, n0);
     if (STATS) {
       sat += s0;
       nan_ += n0;
@@ -418,7 +433,7 @@ __global__ void __launch_bounds__(kHistThreads) k_hist(HistArgs a) {
   const int g = layer_group(a.blob, G, l);
   const float step = blob_step(a.blob, g);
   const float rcp = 1.0f / step;
-  const bool fast = qflag(a.blob, s.L, s.H, s.D, G, g);
+  const int qm = qmode(a.blob, s.L, s.H, s.D, G, g);
   __syncthreads();
 
   const uint16_t* xb = a.x + (((size_t)l * 2 + kv) * s.H + h) * (size_t)s.T * s.D + 64 * j;
@@ -427,17 +442,18 @@ __global__ void __launch_bounds__(kHistThreads) k_hist(HistArgs a) {
   const int t_begin = (int)(s.T * wave / kHistWaves), t_end = (int)(s.T * (wave + 1) / kHistWaves);
   uint32_t sat = 0, nan_ = 0;
   if (t_begin < t_end) {
+#define CG_HIST(QM, ST) \
+  hist_range<QM, ST, BF>(xr, row_bytes, t_begin, t_end, s.C, step, rcp, hist, lane, sat, nan_)
     if (a.stats) {
-      if (fast)
-        hist_range<true, true, BF>(xr, row_bytes, t_begin, t_end, s.C, step, rcp, hist, lane, sat, nan_);
-      else
-        hist_range<false, true, BF>(xr, row_bytes, t_begin, t_end, s.C, step, rcp, hist, lane, sat, nan_);
+      if (qm == kQuotMul) CG_HIST(kQuotMul, true);
+      else if (qm == kQuotFma) CG_HIST(kQuotFma, true);
+      else CG_HIST(kQuotDiv, true);
     } else {
-      if (fast)
-        hist_range<true, false, BF>(xr, row_bytes, t_begin, t_end, s.C, step, rcp, hist, lane, sat, nan_);
-      else
-        hist_range<false, false, BF>(xr, row_bytes, t_begin, t_end, s.C, step, rcp, hist, lane, sat, nan_);
+      if (qm == kQuotMul) CG_HIST(kQuotMul, false);
+      else if (qm == kQuotFma) CG_HIST(kQuotFma, false);
+      else CG_HIST(kQuotDiv, false);
     }
+#undef CG_HIST
   }
   __syncthreads();
   const size_t set = (((size_t)g * 2 + kv) * s.H + h) * s.S + j;
@@ -638,11 +654,11 @@ struct EncTok {
   double r;      // RU(1/f) (S2 read)
 };
 
-template <bool FAST, bool BF>
+template <int QM, bool BF>
 __device__ __forceinline__ void enc_s1(EncTok& k, uint16_t xprev, int32_t& qhi, float step, float rcp,
                                        const uint32_t* ftab, int lane) {
   uint32_t d0 = 0, d1 = 0;
-  const int32_t qlo = quantize<FAST, BF>(xprev, step, rcp, d0, d1);
+  const int32_t qlo = quantize<QM, BF>(xprev, step, rcp, d0, d1);
   k.d16 = (uint32_t)(qhi - qlo);
   const uint32_t sraw = sym_raw(qhi, qlo);
   k.e = ftab[(sraw < 255u ? sraw : 255u) * 64 + lane];
@@ -679,7 +695,7 @@ __device__ __forceinline__ void enc_s3(const EncTok& k, uint32_t& x, uint32_t& P
 // Encodes tokens n-1 .. 1 of a group (backward), then the head. xr covers the
 // group's column of x (row t at byte t * row_bytes), sr its scratch slot of
 // cap words; every access is in bounds by construction.
-template <bool FAST, bool BF>
+template <int QM, bool BF>
 __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, uint32_t row_bytes,
                                              float step, float rcp, const uint32_t* ftab,
                                              const double* rcp_tab, __amdgpu_buffer_rsrc_t sr,
@@ -691,14 +707,14 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
   uint32_t fmin = 0xFFFFFFFFu;
   auto row = [&](int r) { return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, (uint32_t)r * row_bytes, 0); };
   uint32_t d0 = 0, d1 = 0;
-  int32_t qhi = quantize<FAST, BF>(row(n - 1), step, rcp, d0, d1);
+  int32_t qhi = quantize<QM, BF>(row(n - 1), step, rcp, d0, d1);
   if (n >= 3) {
     // a: token in S3, b: in S2, c: in S1. Prologue: token n-1 through S1 and
     // S2, token n-2 through S1.
     EncTok a, b, c;
-    enc_s1<FAST, BF>(a, row(n - 2), qhi, step, rcp, ftab, lane);
+    enc_s1<QM, BF>(a, row(n - 2), qhi, step, rcp, ftab, lane);
     enc_s2(a, rcp_tab, fmin);
-    enc_s1<FAST, BF>(b, row(n - 3), qhi, step, rcp, ftab, lane);
+    enc_s1<QM, BF>(b, row(n - 3), qhi, step, rcp, ftab, lane);
     // tokens i, i-1, ... enter S1 with x of rows i-1, i-2, ...; the rows of
     // the next batch are loaded while the current one is encoded. Offsets
     // stay scalar: a batch of 16 rows all >= 0 needs no clamp; the last one
@@ -722,7 +738,7 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
     load_batch(xv, i);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // as in hist_range
     auto advance = [&](uint16_t xprev) {
-      enc_s1<FAST, BF>(c, xprev, qhi, step, rcp, ftab, lane);
+      enc_s1<QM, BF>(c, xprev, qhi, step, rcp, ftab, lane);
       enc_s2(b, rcp_tab, fmin);
       enc_s3(a, x, P, sr);
       a = b;
@@ -745,7 +761,7 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
     enc_s3(b, x, P, sr);
   } else if (n == 2) {
     EncTok a;
-    enc_s1<FAST, BF>(a, row(0), qhi, step, rcp, ftab, lane);
+    enc_s1<QM, BF>(a, row(0), qhi, step, rcp, ftab, lane);
     enc_s2(a, rcp_tab, fmin);
     enc_s3(a, x, P, sr);
   }
@@ -836,7 +852,7 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
 
   const float step = blob_step(a.blob, g);
   const float rcp = 1.0f / step;
-  const bool fast = qflag(a.blob, s.L, s.H, s.D, G, g);
+  const int qm = qmode(a.blob, s.L, s.H, s.D, G, g);
   const int64_t gpc = groups_per_chunk(s.L, s.H, s.D);
   const uint32_t cap = (uint32_t)a.cap_words;
   bool table_err = false;
@@ -856,12 +872,12 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
     const uint32_t row_bytes = 2u * (uint32_t)s.D;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(xb, (uint32_t)n * row_bytes);
     uint32_t words, start;
-    if (fast)
-      encode_group<true, BF>(xr, (int)n, row_bytes, step, rcp, ftab, rcp_tab, sr, cap, lane, words, start,
-                         table_err);
-    else
-      encode_group<false, BF>(xr, (int)n, row_bytes, step, rcp, ftab, rcp_tab, sr, cap, lane, words, start,
-                          table_err);
+#define CG_ENC(QM) \
+  encode_group<QM, BF>(xr, (int)n, row_bytes, step, rcp, ftab, rcp_tab, sr, cap, lane, words, start, table_err)
+    if (qm == kQuotMul) CG_ENC(kQuotMul);
+    else if (qm == kQuotFma) CG_ENC(kQuotFma);
+    else CG_ENC(kQuotDiv);
+#undef CG_ENC
     if (lane == 0) {
       a.group_words[slot] = words;
       a.group_start[slot] = start;
