@@ -25,7 +25,8 @@ SOURCES = ("csrc/cg_kernels.hip", "csrc/cg_layout.h", "csrc/cg_api.cpp")
 # kernel symbol fragment -> short name used by bench.py
 # (the codec kernels are templates on the element type; one run uses one type)
 KERNELS = {"k_hist": "cg::k_hist<", "k_encode": "cg::k_encode<", "k_decode": "cg::k_decode<false,",
-           "k_decode_paged": "cg::k_decode<true,", "k_write": "cg::k_write(", "k_copy": "cg::k_copy("}
+           "k_decode_paged": "cg::k_decode<true,", "k_write": "cg::k_write(", "k_copy": "cg::k_copy(",
+           "k_attend": "cg::k_attend<"}
 
 
 def source_hash() -> str:
