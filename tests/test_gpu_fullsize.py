@@ -135,3 +135,60 @@ def test_stream_paged():
     print("streamed %d records, %.1f MB in %.2f ms (%.1f GB/s host-to-device incl. decode)" % (
         n, o[-1] / 1e6, ms, o[-1] / ms / 1e6), flush=True)
     assert torch.equal(pool2.view(torch.int16), pool.view(torch.int16))
+
+
+def test_34b_bf16_robust_calibration_tables():
+    """The 34B workload as bfloat16 with robust tables built from its first
+    quarter of tokens only (calibration data), every chunk encoded with them:
+    sampled tables, groups and decoded slices against the oracle."""
+    U.need_gpu()
+    cfg = synth.CONFIGS["34b"]
+    lvd = cfg.levels[0]
+    X16 = synth.generate(cfg)
+    x = U.to_dev(X16).to(torch.bfloat16)
+    del X16
+    Xb = x.cpu().view(torch.int16).numpy().view(np.uint16)
+    print("generated 34b bf16", flush=True)
+    Tc = cfg.tokens // 4
+    shp = C.shape(cfg.layers, cfg.kv_heads, cfg.head_dim, cfg.tokens, cfg.chunk_tokens, C.CG_DTYPE_BF16)
+    cshp = C.shape(cfg.layers, cfg.kv_heads, cfg.head_dim, Tc, cfg.chunk_tokens, C.CG_DTYPE_BF16)
+    lv = U.codec.level_of(lvd)
+    cd = U.codec.Codec(shp)
+    tables = U.codec.Codec(cshp).build_tables(x[:, :, :, :Tc, :].contiguous(), lv, flags=C.CG_TABLES_ROBUST)
+    out, offs = cd.encode(x, lv, tables)
+    assert cd.read_status() == 0
+    refs, n = cd.refs_for(out, offs)
+    y = cd.decode([lv], [tables], refs, n)
+    assert cd.read_status() == 0
+    rng = np.random.default_rng(3)
+    blob = U.u8(tables[:cd.format_bytes(lv)])
+    G = len(lvd.steps)
+    # tables: robust normalisation of the calibration counts
+    Xc = np.ascontiguousarray(Xb[:, :, :, :Tc, :])
+    ocshp = U.O.shape(cfg.layers, cfg.kv_heads, cfg.head_dim, Tc, cfg.chunk_tokens, U.O.BF16)
+    f = U.O.table_f(blob, ocshp, G)
+    for _ in range(4):
+        g, kv, h, d = int(rng.integers(G)), int(rng.integers(2)), int(rng.integers(cfg.kv_heads)), \
+            int(rng.integers(cfg.head_dim))
+        counts, _ = U.O.table_counts(ocshp, lvd.layer_group, lvd.steps, Xc, g, kv, h, d)
+        assert np.array_equal(f[g, kv, h, d], U.O.normalize(counts, robust=True)), (g, kv, h, d)
+    del Xc
+    # groups of the whole tensor coded with the calibration tables
+    oshp = U.O.shape(cfg.layers, cfg.kv_heads, cfg.head_dim, cfg.tokens, cfg.chunk_tokens, U.O.BF16)
+    o = offs.cpu().numpy()
+    S = cfg.head_dim // 64
+    gpc = cfg.layers * 2 * cfg.kv_heads * S
+    for c in [cfg.n_chunks - 1] + [int(rng.integers(cfg.n_chunks)) for _ in range(3)]:
+        l, kv, h, j = (int(rng.integers(cfg.layers)), int(rng.integers(2)), int(rng.integers(cfg.kv_heads)),
+                       int(rng.integers(S)))
+        w = U.O.encode_group(oshp, blob, Xb, c, l, kv, h, j)
+        rec = U.u8(out[int(o[c]):int(o[c + 1])])
+        got = F.record_group(rec, gpc, ((l * 2 + kv) * cfg.kv_heads + h) * S + j)
+        assert np.array_equal(got, w), (c, l, kv, h, j)
+    # decoded slices
+    for _ in range(3):
+        l, kv, h = int(rng.integers(cfg.layers)), int(rng.integers(2)), int(rng.integers(cfg.kv_heads))
+        st = lvd.steps[lvd.layer_group[l]]
+        ref = F.npref.dequantize_bits(F.npref.quantize_bits(Xb[l, kv, h], st, 1), st, 1)
+        assert np.array_equal(y[l, kv, h].cpu().view(torch.int16).numpy().view(np.uint16), ref), (l, kv, h)
+    print("34b bf16 robust ratio %.3f:1" % (2 * Xb.size / int(o[-1])), flush=True)
