@@ -87,7 +87,7 @@ def main():
                          "launch for the FETCH_SIZE / WRITE_SIZE counter runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only; --gpus %d is not supported" % args.gpus,
+        print("bench.py: the codec is measured on one GPU only; --gpus %d is not supported" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 

@@ -59,7 +59,7 @@ extern "C" {
 typedef int32_t cg_status;
 #define CG_OK 0
 #define CG_ERR_INVALID_ARG (-1) /* bad argument, shape, pointer or block-table entry */
-#define CG_ERR_UNSUPPORTED (-2) /* valid but outside this build's limits             */
+#define CG_ERR_UNSUPPORTED (-2) /* valid but outside the library's limits          */
 #define CG_ERR_CAPACITY (-3)    /* output buffer too small (encode)                  */
 #define CG_ERR_HIP (-4)         /* a HIP launch or runtime call failed                */
 #define CG_ERR_CORRUPT (-5)     /* a record or stream failed its integrity checks      */

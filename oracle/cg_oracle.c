@@ -29,7 +29,7 @@
  *
  * The pages fix none of the bit-level choices (rounding, alphabet, escape,
  * normalisation, stream layout). Those are readings, each marked READING
- * below; the build's design notes list them all.
+ * below.
  *
  * Compile: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math (no SIMD code).
  */
