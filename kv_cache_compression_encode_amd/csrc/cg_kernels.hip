@@ -1398,7 +1398,7 @@ __device__ __forceinline__ uint32_t stream_load_async(const Chain& c, uint32_t w
 
 template <int NC>
 __device__ __forceinline__ void ph_a(Chain& c, const uint32_t* tabs, int lane, int it) {
-  if (c.pb > c.lim_b) {  // fewer than 128 words staged
+  if (__builtin_expect(c.pb > c.lim_b, 0)) {  // fewer than 128 words staged
     wait_stream_load<NC>(it - c.pref_it);
     ring_put(c, c.loaded, c.pref, lane);
     c.loaded += kRingBlock;
@@ -1433,8 +1433,10 @@ __device__ __forceinline__ void ph_d(const DecodeArgs& a, Chain& c, int i, int h
   renorm_lanes(c.x, c.w, c.mr);
   add_twice(c.pb, (uint32_t)__popcll(c.mr));
   c.q += (uint32_t)(int32_t)(int8_t)(c.info & 0xFFu);
+  // escapes and refills are rare: as unlikely branches their blocks leave
+  // the loop's straight path, which then takes no branch
   const uint64_t me = __ballot((c.info & 0xFFu) == 0x80u);
-  if (me) {
+  if (__builtin_expect(me != 0, 0)) {
     const uint16_t* ep = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(c.ring) +
                                                             (c.pb & (2u * kRingWords - 1)));
     if ((c.info & 0xFFu) == 0x80u) c.q += 128u + ep[mbcnt_base(me, 0)];
