@@ -1148,7 +1148,7 @@ __device__ __forceinline__ uint32_t row_offset(const DecodeArgs& a, Chain& c, in
                                                uint32_t row_bytes, int lane) {
   if (!PAGED) return (uint32_t)(t - c.t0) * row_bytes;
   const int64_t b = (t >> 4) - c.bt_base;
-  if (b >= 128) {  // next window of 128 block-table entries
+  if (__builtin_expect(b >= 128, 0)) {  // next window of 128 block-table entries
     c.bt_base += 128;
     const int64_t i0 = c.bt_base + lane, i1 = c.bt_base + 64 + lane;
     const int64_t last = (c.t0 + c.n - 1) >> 4;
@@ -1170,7 +1170,7 @@ __device__ __forceinline__ uint32_t row_offset(const DecodeArgs& a, Chain& c, in
 template <bool PAGED>
 __device__ __forceinline__ void next_row(const DecodeArgs& a, Chain& c, int i, int h, uint32_t row_bytes,
                                          int lane) {
-  if (!PAGED || c.pg_left != 0) {
+  if (!PAGED || __builtin_expect(c.pg_left != 0, 1)) {  // page boundaries: 1 token in 16
     c.doff += row_bytes;
     if (PAGED) c.pg_left -= 1;
   } else {
