@@ -48,3 +48,31 @@ def test_binding_names_match_header():
     for name in declared():
         assert hasattr(C, name), name
     assert set(C.EXPORTS) == set(declared())
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="libcg.so not built")
+def test_argument_checks_before_any_launch():
+    """Calls that fail validation return before touching the GPU, so these
+    run without one: bad shapes, element types, flags and attention limits."""
+    from kv_cache_compression_encode_amd import cg as C
+    ok = C.shape(4, 2, 64, 1024, 256)
+    assert C.cg_tables_bytes(C.shape(4, 2, 64, 0, 256), 3) == 0                 # no tokens
+    assert C.cg_tables_bytes(C.shape(4, 2, 64, 1024, 256, dtype=2), 3) == 0     # unknown element type
+    bad = C.shape(4, 2, 64, 1024, 256)
+    bad.reserved = 1
+    assert C.cg_tables_bytes(bad, 3) == 0
+    assert C.cg_tables_bytes(ok, 0) == 0 and C.cg_tables_bytes(ok, 256) == 0    # group count
+    # attention: q_heads a multiple of kv_heads, at most 16 per kv head, D in {64, 128, 256}
+    assert C.cg_attend_workspace_bytes(ok, 4, 100) > 0
+    assert C.cg_attend_workspace_bytes(ok, 3, 100) == 0
+    assert C.cg_attend_workspace_bytes(ok, 34, 100) == 0
+    assert C.cg_attend_workspace_bytes(ok, 4, 0) == 0
+    assert C.cg_attend_workspace_bytes(C.shape(4, 2, 192, 1024, 256), 4, 100) == 0
+    # unknown table flags are refused before the first launch
+    lv = C.Level(0, [0, 0, 1, 1], [0.5, 1.0])
+    L = C.lib()
+    rc = L.cg_build_tables(C.ctypes.byref(ok), C.ctypes.byref(lv.c), 256, 256, 256, 1 << 20, 2, None, None, None)
+    assert rc == C.CG_ERR_INVALID_ARG
+    # decoders: no levels
+    rc = L.cg_decode(C.ctypes.byref(ok), 0, None, None, None, 1, None, None, None, None)
+    assert rc == C.CG_ERR_INVALID_ARG

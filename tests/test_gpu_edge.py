@@ -1,0 +1,66 @@
+"""Edge cases of the codec on the GPU against the oracle, byte by byte:
+every fp16 bit pattern (NaN, +-Inf, subnormals, saturation), a tensor where
+every delta needs an escape (the worst-case stream size), one layer group per
+layer, and the largest group count (255)."""
+import numpy as np
+import pytest
+
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+def every_fp16_pattern():
+    k = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(1024, 64)
+    return np.stack([k, k[::-1, ::-1]])[None, :, None].copy().view(np.float16)
+
+
+def all_escapes():
+    rng = np.random.default_rng(61)
+    return rng.uniform(-60000, 60000, size=(2, 2, 1, 300, 64)).astype(np.float16)
+
+
+def many_groups(L, T, seed):
+    from kv_cache_compression_encode_amd import synth
+    return synth.random_kv(L, 1, 64, T, seed, scale=5.0)
+
+
+CASES = [
+    # name, L, H, D, T, C, layer_group, steps, X
+    ("every-fp16-pattern", 1, 1, 64, 1024, 256, [0], [0.37], every_fp16_pattern),
+    ("all-escapes", 2, 1, 64, 300, 100, [0, 0], [4.0], all_escapes),
+    ("group-per-layer", 64, 1, 64, 40, 16, list(range(64)), [0.3 + 0.025 * g for g in range(64)],
+     lambda: many_groups(64, 40, 62)),
+    ("255-groups", 255, 1, 64, 12, 5, list(range(255)), [0.5 + 0.01 * g for g in range(255)],
+     lambda: many_groups(255, 12, 63)),
+]
+
+
+@pytest.fixture(scope="module", params=CASES, ids=[c[0] for c in CASES])
+def pair(request):
+    U.need_gpu()
+    name, L, H, D, T, Cc, lg, steps, mk = request.param
+    X = mk()
+    print("case", name, flush=True)
+    args = (L, H, D, T, Cc, lg, steps, X, 11)
+    return name, U.gpu_roundtrip(*args), U.oracle_roundtrip(*args)
+
+
+def test_tables_and_stats(pair):
+    name, g, o = pair
+    fb = len(o["blob"])
+    assert np.array_equal(U.u8(g["tables"])[:fb], o["blob"])
+    assert np.array_equal(g["stats"].cpu().numpy().astype(np.uint64), o["stats"])
+    if name == "every-fp16-pattern":
+        assert int(o["stats"][2]) == 2 * 2046  # every NaN pattern, in K and in V
+    if name == "all-escapes":
+        assert int(o["stats"][3]) > 0.95 * 2 * 2 * 299 * 64
+
+
+def test_records_and_decode(pair):
+    name, g, o = pair
+    assert g["st_enc"] == 0 and g["st_dec"] == 0
+    offs = g["offs"].cpu().numpy().astype(np.uint64)
+    assert np.array_equal(offs, o["offs"])
+    assert np.array_equal(U.u8(g["out"])[:int(offs[-1])], o["data"])
+    assert np.array_equal(g["y"].cpu().numpy().view(np.uint16), o["Y"])
