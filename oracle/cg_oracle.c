@@ -589,10 +589,9 @@ done:
 }
 
 /* Inverse of the above. Writes q[64][n]. Returns CGO_OK or CGO_ERR_CORRUPT
- * (a word read past the end, a final state other than 2^16, words left, or
- * an escape in a group whose record says it has none: allow_esc = 0). */
-static int decode_group_impl(const uint16_t* w, int64_t n_words, int64_t n,
-                             const uint16_t* const f_lane[64], int32_t* q, int allow_esc) {
+ * (a word read past the end, a final state other than 2^16, or words left). */
+int cgo_decode_group_q(const uint16_t* w, int64_t n_words, int64_t n,
+                       const uint16_t* const f_lane[64], int32_t* q /* [64][n] */) {
   uint32_t b[64][256];
   for (int k = 0; k < CGO_LANES; k++) cumulative(f_lane[k], b[k]);
   if (n_words < CGO_HDR_WORDS) return CGO_ERR_CORRUPT;
@@ -623,7 +622,7 @@ static int decode_group_impl(const uint16_t* w, int64_t n_words, int64_t n,
     for (int k = 0; k < CGO_LANES; k++) {
       int32_t d;
       if (sym[k] == CGO_ESC) {
-        if (!allow_esc || p >= n_words) return CGO_ERR_CORRUPT;
+        if (p >= n_words) return CGO_ERR_CORRUPT;
         d = (int16_t)w[p++];
       } else {
         d = sym[k] - 127;
@@ -635,23 +634,6 @@ static int decode_group_impl(const uint16_t* w, int64_t n_words, int64_t n,
     if (x[k] != CGO_L) return CGO_ERR_CORRUPT;
   if (p != n_words) return CGO_ERR_CORRUPT;
   return CGO_OK;
-}
-
-int cgo_decode_group_q(const uint16_t* w, int64_t n_words, int64_t n,
-                       const uint16_t* const f_lane[64], int32_t* q /* [64][n] */) {
-  return decode_group_impl(w, n_words, n, f_lane, q, 1);
-}
-
-/* Does the group code any escape (so its record flags it)? The symbol rule
- * of the encoder above, applied without coding. */
-static int group_has_escape(const int32_t* q, int64_t n, const uint16_t* const f_lane[64], int robust) {
-  for (int k = 0; k < CGO_LANES; k++)
-    for (int64_t i = 1; i < n; i++) {
-      uint16_t pay;
-      int sym = symbol_of(cgo_wrap16(q[k * n + i] - q[k * n + i - 1]), &pay);
-      if (sym == CGO_ESC || (robust && f_lane[k][sym] == 0)) return 1;
-    }
-  return 0;
 }
 
 static void lane_tables(const cgo_shape* s, const blob_view* v, int l, int kv, int h, int j,
@@ -691,9 +673,7 @@ int64_t cgo_encode_group(const cgo_shape* s, const uint8_t* blob, const uint16_t
 /*  16 token_start (u64)  24 n_tokens  28 n_groups  32 layers  36 kv_heads   */
 /*  40 head_dim  44 data_start  48 record_bytes (u64)  56 data_bytes (u64)   */
 /*  64 u64 group_offset[n_groups+1] (from data start, multiples of 16)       */
-/*     u32 group_words[n_groups] (bit 31: the group codes escapes; READING:  */
-/*     decoders then know which groups need the escape test); zero pad to    */
-/*     data_start (align 256);                                               */
+/*     u32 group_words[n_groups]; zero pad to data_start (align 256);        */
 /*     group streams in (layer, K|V, head, slice) order, each zero-padded to */
 /*     16 bytes; zero pad to record_bytes (align 256).                        */
 /* ------------------------------------------------------------------------ */
@@ -747,7 +727,7 @@ int64_t cgo_encode_chunk(const cgo_shape* s, const uint8_t* blob, const uint16_t
             data_cap *= 2;
           }
           offs[gi] = pos;
-          nw[gi] = (uint32_t)m | (group_has_escape(q, n, f_lane, v->robust) ? 0x80000000u : 0u);
+          nw[gi] = (uint32_t)m;
           for (int64_t k = 0; k < m; k++) put_u16(data + pos + 2 * k, words[k]);
           pos += padded;
         }
@@ -824,7 +804,7 @@ static int check_record(const cgo_shape* s, const blob_view* v, const uint8_t* r
     if (g == 0 && o != 0) return CGO_ERR_CORRUPT;
     if (g == G && o != db) return CGO_ERR_CORRUPT;
     if (g > 0) {
-      uint64_t nw = get_u32(rec + 64 + 8 * (G + 1) + 4 * (g - 1)) & 0x7FFFFFFFu;
+      uint64_t nw = get_u32(rec + 64 + 8 * (G + 1) + 4 * (g - 1));
       if (2 * nw > o - prev) return CGO_ERR_CORRUPT;
     }
     prev = o;
@@ -872,12 +852,11 @@ static int decode_chunk_impl(const cgo_shape* s, const uint8_t* blob, const uint
       for (int h = 0; h < H && rc == CGO_OK; h++)
         for (int j = 0; j < slices && rc == CGO_OK; j++, gi++) {
           uint64_t o = get_u64(rec + 64 + 8 * gi);
-          uint32_t nwf = get_u32(rec + 64 + 8 * (G + 1) + 4 * gi);
-          uint64_t nw = nwf & 0x7FFFFFFFu;
+          uint64_t nw = get_u32(rec + 64 + 8 * (G + 1) + 4 * gi);
           words = (uint16_t*)realloc(words, sizeof(uint16_t) * (size_t)(nw + 1));
           for (uint64_t k = 0; k < nw; k++) words[k] = get_u16(rec + ds + o + 2 * k);
           lane_tables(s, v, l, kv, h, j, fbuf, f_lane);
-          rc = decode_group_impl(words, (int64_t)nw, n, f_lane, q, (int)(nwf >> 31));
+          rc = cgo_decode_group_q(words, (int64_t)nw, n, f_lane, q);
           if (rc != CGO_OK) break;
           float step = v->steps[v->lg[l]];
           for (int k = 0; k < CGO_LANES; k++)
