@@ -1661,7 +1661,10 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
   __syncthreads();
 
   // items = (record, k-th layer of the group), record-major; wavefront w
-  // takes items w, w + 16, w + 32
+  // takes items w, w + 16, w + 32. Deeper layers code more bits per value, so
+  // the layer order is turned around in the second record and rotated by half
+  // in the third: each wavefront gets a shallow, a deep and a middle layer
+  // rather than the same depth three times.
   const int items = nrec * lg_count;
   const int mine = wave < items ? (items - 1 - wave) / kWaves + 1 : 0;
   if (mine == 0) return;
@@ -1672,7 +1675,10 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
       const int it = wave + k * kWaves;
       const int ri = it / lg_count;
       GroupRef gr = ri == 0 ? rr0 : ri == 1 ? rr1 : rr2;
-      gr.l = layer_of_group(blob, G, s.L, g, it - ri * lg_count, lane);
+      int li = it - ri * lg_count;
+      if (ri == 1) li = lg_count - 1 - li;
+      if (ri == 2) li = (li + lg_count / 2) % lg_count;
+      gr.l = layer_of_group(blob, G, s.L, g, li, lane);
       chain_open<PAGED, BF>(a, c[k], gr, gpc, kv, h, j, step, rings + (wave * kChains + k) * kRingStride,
                         lane);
     } else {
