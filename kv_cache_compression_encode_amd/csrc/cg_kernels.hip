@@ -201,6 +201,39 @@ __device__ __forceinline__ T* uni(T* p) {
   return reinterpret_cast<T*>(uni((uint64_t)reinterpret_cast<uintptr_t>(p)));
 }
 
+// ---- wavefront priority from progress ---------------------------------------
+// A SIMD issues from its oldest ready wavefront first. In the encoder and
+// decoder a workgroup of 16 wavefronts owns the CU (its tables fill the LDS)
+// and every wavefront has the same amount of work, so under age order the
+// four wavefronts of a SIMD finish one after another, the last ~20 % behind
+// the mean and alone on its SIMD at the end, while the workgroup's LDS stays
+// held. Each wavefront therefore publishes the tokens it has left in an LDS
+// slot every 32 tokens and raises its priority by the number of its SIMD's
+// other wavefronts (of its workgroup) with fewer left. Wavefront w runs on
+// the SIMD of w + 4, w + 8, ... (the dispatcher's order, measured); were it
+// otherwise the priorities would only balance less, never change a result.
+// The histogram workgroups (8 wavefronts, two per CU) do the same with their
+// one SIMD-mate; they gain less, since the other workgroup fills the SIMD.
+constexpr int kProgressPeriod = 32;  // tokens between two updates (a power of two)
+
+__device__ __forceinline__ void set_priority(int p) {
+  if (p <= 0) __builtin_amdgcn_s_setprio(0);
+  else if (p == 1) __builtin_amdgcn_s_setprio(1);
+  else if (p == 2) __builtin_amdgcn_s_setprio(2);
+  else __builtin_amdgcn_s_setprio(3);
+}
+
+// left[WAVES]: tokens each wavefront of the workgroup has left (LDS). Entries
+// are read without synchronisation; a stale value only delays the balance.
+template <int WAVES>
+__device__ __forceinline__ void publish_progress(int* left, int wave, int mine, int lane) {
+  static_assert(WAVES == 8 || WAVES == 16, "two or four wavefronts per SIMD");
+  if (lane == 0) left[wave] = mine;
+  int ahead = uni(left[wave ^ 4]) < mine;
+  if (WAVES == 16) ahead += (uni(left[wave ^ 8]) < mine) + (uni(left[wave ^ 12]) < mine);
+  set_priority(ahead);
+}
+
 // Raw buffer resource over [base, base + bytes): accesses use a per-lane
 // offset in a VGPR plus a wave-uniform offset in an SGPR, so address
 // arithmetic stays on the scalar unit. The hardware range check covers the
@@ -354,7 +387,8 @@ constexpr int kHistBatch = 16;
 template <int QM, bool STATS, bool BF>
 __device__ __forceinline__ void hist_range(__amdgpu_buffer_rsrc_t xr, uint32_t row_bytes, int t_begin,
                                            int t_end, int C, float step, float rcp, uint32_t* hist,
-                                           int lane, uint32_t& sat, uint32_t& nan_) {
+                                           int* left, int wave, int lane, uint32_t& sat,
+                                           uint32_t& nan_) {
   const uint32_t lane2 = 2u * lane;
   uint32_t* hl = hist + lane;
   int32_t prev = 0;
@@ -402,7 +436,9 @@ __device__ __forceinline__ void hist_range(__amdgpu_buffer_rsrc_t xr, uint32_t r
   // the first batch lands before the loop: otherwise its pending loads merge
   // into the loop's wait counts and every token waits on the next batch
   __builtin_amdgcn_s_waitcnt(0x0F70);
+  static_assert(2 * kHistBatch == kProgressPeriod, "progress every second batch");
   for (; t + kHistBatch <= t_end; t += kHistBatch) {
+    if (((t - t_begin) & kHistBatch) == 0) publish_progress<kHistWaves>(left, wave, t_end - t, lane);
     uint32_t xn[kHistBatch];
     load_batch(xn, t + kHistBatch);
 #pragma unroll
@@ -418,8 +454,10 @@ __device__ __forceinline__ void hist_range(__amdgpu_buffer_rsrc_t xr, uint32_t r
 template <bool BF>
 __global__ void __launch_bounds__(kHistThreads) k_hist(HistArgs a) {
   __shared__ uint32_t hist[257 * 64];
+  __shared__ int left[kHistWaves];  // tokens each wavefront has left (priorities)
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   for (int i = tid; i < 257 * 64; i += kHistThreads) hist[i] = 0;
+  if (tid < kHistWaves) left[tid] = 0x7FFFFFFF;
 
   const Shape s = a.s;
   int64_t bid = blockIdx.x;
@@ -443,7 +481,7 @@ __global__ void __launch_bounds__(kHistThreads) k_hist(HistArgs a) {
   uint32_t sat = 0, nan_ = 0;
   if (t_begin < t_end) {
 #define CG_HIST(QM, ST) \
-  hist_range<QM, ST, BF>(xr, row_bytes, t_begin, t_end, s.C, step, rcp, hist, lane, sat, nan_)
+  hist_range<QM, ST, BF>(xr, row_bytes, t_begin, t_end, s.C, step, rcp, hist, left, wave, lane, sat, nan_)
     if (a.stats) {
       if (qm == kQuotMul) CG_HIST(kQuotMul, true);
       else if (qm == kQuotFma) CG_HIST(kQuotFma, true);
@@ -700,7 +738,8 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
                                              float step, float rcp, const uint32_t* ftab,
                                              const double* rcp_tab, __amdgpu_buffer_rsrc_t sr,
                                              uint32_t cap, int lane, uint32_t& words,
-                                             uint32_t& start, bool& table_err) {
+                                             uint32_t& start, bool& table_err, int* left, int wave,
+                                             int left_after) {
   const uint32_t lane2 = 2u * lane;
   uint32_t P = cap;
   uint32_t x = kL;
@@ -744,7 +783,9 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
       a = b;
       b = c;
     };
+    static_assert(2 * kEncBatch == kProgressPeriod, "progress every second batch");
     for (; i >= kEncBatch; i -= kEncBatch) {
+      if (i & kEncBatch) publish_progress<kWaves>(left, wave, left_after + i, lane);
       uint32_t xn[kEncBatch];
       load_batch(xn, i - kEncBatch);
 #pragma unroll
@@ -811,6 +852,7 @@ constexpr int kEncFtabOff = (kEncRcpBytes + 255) / 256 * 256;
 template <bool BF>
 __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
   __shared__ __align__(16) uint8_t enc_lds[kEncFtabOff + 4 * kEncDwords * 64];
+  __shared__ int left[kWaves];
   double* rcp_tab = reinterpret_cast<double*>(enc_lds);
   uint32_t* ftab = reinterpret_cast<uint32_t*>(enc_lds + kEncFtabOff);
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -848,6 +890,7 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
     rcp_tab[f] = r;
   }
   if (tid == 0) rcp_tab[0] = 0.0;
+  if (tid < kWaves) left[tid] = 0x7FFFFFFF;
   __syncthreads();
 
   const float step = blob_step(a.blob, g);
@@ -860,10 +903,14 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
   // items w, w + 16, ...
   const int lg_count = layers_in_group(a.blob, G, s.L, g, lane);
   const int items = (int)(cl_end - cl_begin) * lg_count;
+  int my_left = 0;  // tokens of this wavefront's groups not yet encoded
+  for (int it = wave; it < items; it += kWaves)
+    my_left += (int)chunk_len(s.T, s.C, a.chunk_begin + cl_begin + it / lg_count);
   for (int it = wave; it < items; it += kWaves) {
     const int64_t cl = cl_begin + it / lg_count;  // chunk index within the call
     const int64_t c = a.chunk_begin + cl;
     const int64_t n = chunk_len(s.T, s.C, c), t0 = c * s.C;
+    my_left -= (int)n;
     const int l = layer_of_group(a.blob, G, s.L, g, it % lg_count, lane);
     const int64_t gi = (((int64_t)l * 2 + kv) * s.H + h) * s.S + j;
     const int64_t slot = cl * gpc + gi;
@@ -873,7 +920,8 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(xb, (uint32_t)n * row_bytes);
     uint32_t words, start;
 #define CG_ENC(QM) \
-  encode_group<QM, BF>(xr, (int)n, row_bytes, step, rcp, ftab, rcp_tab, sr, cap, lane, words, start, table_err)
+  encode_group<QM, BF>(xr, (int)n, row_bytes, step, rcp, ftab, rcp_tab, sr, cap, lane, words, start, table_err, \
+               left, wave, my_left)
     if (qm == kQuotMul) CG_ENC(kQuotMul);
     else if (qm == kQuotFma) CG_ENC(kQuotFma);
     else CG_ENC(kQuotDiv);
@@ -883,6 +931,7 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
       a.group_start[slot] = start;
     }
   }
+  if (lane == 0) left[wave] = 0;
   if (__ballot(table_err) && lane == 0) set_status(a.status, CG_ERR_TABLE);
 }
 
@@ -1457,7 +1506,8 @@ __device__ __forceinline__ void ph_d(const DecodeArgs& a, Chain& c, int i, int h
 // issued (the compiler would sink the reads to the end of a slot).
 template <bool PAGED, int NC, bool BF>
 __device__ __forceinline__ void chain_pipe(const DecodeArgs& a, Chain* c, int i0, int i1,
-                                           const uint32_t* tabs, int h, float step, int lane) {
+                                           const uint32_t* tabs, int* left, int h, float step,
+                                           int lane) {
   static_assert(NC == 2 || NC == 3, "two or three chains");
   const uint32_t row_bytes = 2u * (uint32_t)a.s.D;
   // see chain_steps: no load of an earlier loop may stay pending; the
@@ -1486,7 +1536,9 @@ __device__ __forceinline__ void chain_pipe(const DecodeArgs& a, Chain* c, int i0
     CG_SLOT;
   }
   int it = 1;
+  const int wave = wave_id();
   for (int i = i0; i < i1 - 1; ++i, ++it) {
+    if ((i & (kProgressPeriod - 1)) == 0) publish_progress<kWaves>(left, wave, i1 - i, lane);
     ph_d<PAGED, BF>(a, c[0], i, h, step, row_bytes, lane);
     ph_a<NC>(c[0], tabs, lane, it);
     CG_SLOT;
@@ -1534,7 +1586,7 @@ __device__ __forceinline__ void chain_pipe(const DecodeArgs& a, Chain* c, int i0
 // NC chains decoded together for their common length, then the longer ones
 // finish one at a time.
 template <bool PAGED, int NC, bool BF>
-__device__ __forceinline__ void run_chains(const DecodeArgs& a, Chain* c, const uint32_t* tabs,
+__device__ __forceinline__ void run_chains(const DecodeArgs& a, Chain* c, const uint32_t* tabs, int* left,
                                            int h, float step, int lane) {
   int nmin = c[0].n;
 #pragma unroll
@@ -1542,7 +1594,7 @@ __device__ __forceinline__ void run_chains(const DecodeArgs& a, Chain* c, const 
   if constexpr (NC == 1) {
     chain_steps<PAGED, 1, BF>(a, c, 1, nmin, tabs, h, step, lane);
   } else {
-    if (nmin > 1) chain_pipe<PAGED, NC, BF>(a, c, 1, nmin, tabs, h, step, lane);
+    if (nmin > 1) chain_pipe<PAGED, NC, BF>(a, c, 1, nmin, tabs, left, h, step, lane);
   }
   if constexpr (NC > 1) {
 #pragma unroll
@@ -1557,6 +1609,7 @@ template <bool PAGED, bool BF>
 __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
   __shared__ uint32_t tabs[kDecDwords * 64];
   __shared__ uint16_t rings[kWaves * kChains * kRingStride];
+  __shared__ int left[kWaves];  // tokens each wavefront has left (priorities)
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const Shape s = a.s;
   int64_t bid = blockIdx.x;
@@ -1658,6 +1711,7 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
   for (int u = tid; u < kDecDwords * 64 / 4; u += kDecThreads) reinterpret_cast<uint4*>(tabs)[u] = dsrc[u];
   const int lg_count = layers_in_group(blob, G, s.L, g, lane);
   const float step = blob_step(blob, g);
+  if (tid < kWaves) left[tid] = 0x7FFFFFFF;
   __syncthreads();
 
   // items = (record, k-th layer of the group), record-major; wavefront w
@@ -1667,7 +1721,10 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
   // rather than the same depth three times.
   const int items = nrec * lg_count;
   const int mine = wave < items ? (items - 1 - wave) / kWaves + 1 : 0;
-  if (mine == 0) return;
+  if (mine == 0) {
+    if (lane == 0) left[wave] = 0;
+    return;
+  }
   Chain c[kChains];
 #pragma unroll
   for (int k = 0; k < kChains; ++k) {
@@ -1687,15 +1744,16 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
   }
   const bool all_ok = c[0].ok && (mine < 2 || c[1].ok) && (mine < 3 || c[2].ok);
   if (all_ok && mine == 3) {
-    run_chains<PAGED, 3, BF>(a, c, tabs, h, step, lane);
+    run_chains<PAGED, 3, BF>(a, c, tabs, left, h, step, lane);
   } else if (all_ok && mine == 2) {
-    run_chains<PAGED, 2, BF>(a, c, tabs, h, step, lane);
+    run_chains<PAGED, 2, BF>(a, c, tabs, left, h, step, lane);
   } else {
     // one chain, or a damaged directory entry among them: the rest one by one
 #pragma unroll
     for (int k = 0; k < kChains; ++k)
-      if (c[k].ok) run_chains<PAGED, 1, BF>(a, &c[k], tabs, h, step, lane);
+      if (c[k].ok) run_chains<PAGED, 1, BF>(a, &c[k], tabs, left, h, step, lane);
   }
+  if (lane == 0) left[wave] = 0;
 }
 
 // ---------------------------------------------------------------------------
