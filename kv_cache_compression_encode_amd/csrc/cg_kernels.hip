@@ -1171,7 +1171,7 @@ struct Chain {
   uint32_t x, q;               // per lane: rANS state, token value mod 2^16
   int64_t t0;
   int n;
-  uint32_t bt0, bt1;           // paged: block-table entries of blocks bt_base + lane, + 64
+  uint32_t bt0, bt1;           // paged: byte offsets of the pages of blocks bt_base + lane, + 64
   int64_t bt_base;
   uint32_t pg_left;            // paged: tokens left in the current page after the last stored one
   bool ok;
@@ -1192,6 +1192,28 @@ struct GroupRef {
   int l;
 };
 
+// Byte offset in the (layer, K|V) slab of the pool of the first row of head
+// h in the page of block-table entry i (0 past the chain's last block).
+__device__ __forceinline__ uint32_t page_offset(const DecodeArgs& a, int64_t i, int64_t last, int h,
+                                                uint32_t row_bytes) {
+  if (i > last) return 0u;
+  const uint32_t blk = (uint32_t)a.block_table[i];
+  return (blk * (uint32_t)a.s.H + (uint32_t)h) * 16u * row_bytes;
+}
+
+// The chain's window of 128 block-table entries from bt_base on, as page
+// offsets in two registers (entry bt_base + lane, + 64).
+__device__ __forceinline__ void load_pages(const DecodeArgs& a, Chain& c, int h, uint32_t row_bytes, int lane) {
+  const int64_t last = (c.t0 + c.n - 1) >> 4;
+  c.bt0 = page_offset(a, c.bt_base + lane, last, h, row_bytes);
+  c.bt1 = page_offset(a, c.bt_base + 64 + lane, last, h, row_bytes);
+}
+
+__device__ __forceinline__ uint32_t page_in_window(const Chain& c, uint32_t bi) {
+  return bi < 64 ? (uint32_t)__builtin_amdgcn_readlane(c.bt0, bi)
+                 : (uint32_t)__builtin_amdgcn_readlane(c.bt1, bi - 64);
+}
+
 template <bool PAGED>
 __device__ __forceinline__ uint32_t row_offset(const DecodeArgs& a, Chain& c, int64_t t, int h,
                                                uint32_t row_bytes, int lane) {
@@ -1199,18 +1221,12 @@ __device__ __forceinline__ uint32_t row_offset(const DecodeArgs& a, Chain& c, in
   const int64_t b = (t >> 4) - c.bt_base;
   if (__builtin_expect(b >= 128, 0)) {  // next window of 128 block-table entries
     c.bt_base += 128;
-    const int64_t i0 = c.bt_base + lane, i1 = c.bt_base + 64 + lane;
-    const int64_t last = (c.t0 + c.n - 1) >> 4;
-    c.bt0 = i0 <= last ? (uint32_t)a.block_table[i0] : 0u;
-    c.bt1 = i1 <= last ? (uint32_t)a.block_table[i1] : 0u;
+    load_pages(a, c, h, row_bytes, lane);
     // wait here, once per 2048 tokens, so the compiler does not have to
     // assume these loads pending (and wait for every store) on each step
     __builtin_amdgcn_s_waitcnt(0x0F70);
   }
-  const uint32_t bi = (uint32_t)((t >> 4) - c.bt_base);
-  const uint32_t blk = bi < 64 ? (uint32_t)__builtin_amdgcn_readlane(c.bt0, bi)
-                               : (uint32_t)__builtin_amdgcn_readlane(c.bt1, bi - 64);
-  return ((blk * (uint32_t)a.s.H + (uint32_t)h) * 16u + (uint32_t)(t & 15)) * row_bytes;
+  return page_in_window(c, (uint32_t)((t >> 4) - c.bt_base)) + (uint32_t)(t & 15) * row_bytes;
 }
 
 // Output row of token i of the chain, from the previous one: the next row of
@@ -1285,10 +1301,7 @@ __device__ __forceinline__ void chain_open(const DecodeArgs& a, Chain& c, const 
     const uint16_t* p0 = a.pool + ((size_t)gr.l * 2 + kv) * (size_t)a.num_blocks * s.H * 16 * s.D + col;
     c.dst = make_rsrc(p0, (uint32_t)((uint64_t)a.num_blocks * s.H * 16 * row_bytes));
     c.bt_base = gr.t0 >> 4;
-    const int64_t last = (gr.t0 + gr.n - 1) >> 4;
-    const int64_t i0 = c.bt_base + lane, i1 = c.bt_base + 64 + lane;
-    c.bt0 = i0 <= last ? (uint32_t)a.block_table[i0] : 0u;
-    c.bt1 = i1 <= last ? (uint32_t)a.block_table[i1] : 0u;
+    load_pages(a, c, h, row_bytes, lane);
   }
   c.doff = row_offset<PAGED>(a, c, gr.t0, h, row_bytes, lane);
   c.pg_left = 15u - (uint32_t)(gr.t0 & 15);
@@ -1476,7 +1489,7 @@ __device__ __forceinline__ void ph_c(Chain& c) {
   c.w = rp[mbcnt_base(c.mr, 0)];  // every lane reads; only renormalising lanes use it
 }
 
-template <bool PAGED, bool BF>
+template <bool PAGED, bool BF, bool ADV = true>
 __device__ __forceinline__ void ph_d(const DecodeArgs& a, Chain& c, int i, int h, float step,
                                      uint32_t row_bytes, int lane) {
   renorm_lanes(c.x, c.w, c.mr);
@@ -1492,11 +1505,43 @@ __device__ __forceinline__ void ph_d(const DecodeArgs& a, Chain& c, int i, int h
     add_twice(c.pb, (uint32_t)__popcll(me));
   }
   const uint16_t y = dequantize_low16<BF>(c.q, step);
-  if (PAGED)
-    next_row<PAGED>(a, c, i, h, row_bytes, lane);
-  else
-    c.doff += row_bytes;
+  if (ADV) {
+    if (PAGED)
+      next_row<PAGED>(a, c, i, h, row_bytes, lane);
+    else
+      c.doff += row_bytes;
+  }
   __builtin_amdgcn_raw_buffer_store_b16(y, c.dst, 2u * lane, c.doff, 0);
+}
+
+// Paged output of NC chains whose pages start at the same token offset (the
+// chunk length a multiple of 16, or equal starts): one page counter for all,
+// and every chain's row advanced at the top of the step, instead of a test
+// per chain per token.
+// pg: tokens left in the current page; bi: the page's index in the chains'
+// windows (the same for all: their pages start at the same offset).
+template <int NC>
+__device__ __forceinline__ void next_rows_in_step(const DecodeArgs& a, Chain* c, int h, uint32_t row_bytes,
+                                                  uint32_t& pg, uint32_t& bi, int lane) {
+  if (__builtin_expect(pg != 0, 1)) {
+#pragma unroll
+    for (int k = 0; k < NC; ++k) c[k].doff += row_bytes;
+    pg -= 1;
+  } else {
+    bi += 1;
+    if (__builtin_expect(bi == 128, 0)) {  // next windows of 128 block-table entries
+#pragma unroll
+      for (int k = 0; k < NC; ++k) {
+        c[k].bt_base += 128;
+        load_pages(a, c[k], h, row_bytes, lane);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // as in row_offset
+      bi = 0;
+    }
+#pragma unroll
+    for (int k = 0; k < NC; ++k) c[k].doff = page_in_window(c[k], bi);  // row 0 of the page
+    pg = 15;
+  }
 }
 
 #define CG_SLOT __builtin_amdgcn_sched_barrier(0)
@@ -1504,11 +1549,15 @@ __device__ __forceinline__ void ph_d(const DecodeArgs& a, Chain& c, int i, int h
 // Tokens [i0, i1) of NC = 2 or 3 chains, i1 > i0, software-pipelined. A
 // scheduling fence after every phase keeps each phase's LDS read where it is
 // issued (the compiler would sink the reads to the end of a slot).
-template <bool PAGED, int NC, bool BF>
+template <bool PAGED, int NC, bool BF, bool SYNC>
 __device__ __forceinline__ void chain_pipe(const DecodeArgs& a, Chain* c, int i0, int i1,
                                            const uint32_t* tabs, int* left, int h, float step,
                                            int lane) {
   static_assert(NC == 2 || NC == 3, "two or three chains");
+  static_assert(PAGED || !SYNC, "one page counter: paged output only");
+  constexpr bool ADV = !SYNC;  // the row advance: in ph_d, or for all chains per step
+  uint32_t pg = SYNC ? c[0].pg_left : 0u;
+  uint32_t bi = SYNC ? (uint32_t)(((c[0].t0 + i0 - 1) >> 4) - c[0].bt_base) : 0u;
   const uint32_t row_bytes = 2u * (uint32_t)a.s.D;
   // see chain_steps: no load of an earlier loop may stay pending; the
   // compiler-issued prefetch of chain_open is complete after this wait
@@ -1539,7 +1588,8 @@ __device__ __forceinline__ void chain_pipe(const DecodeArgs& a, Chain* c, int i0
   const int wave = wave_id();
   for (int i = i0; i < i1 - 1; ++i, ++it) {
     if ((i & (kProgressPeriod - 1)) == 0) publish_progress<kWaves>(left, wave, i1 - i, lane);
-    ph_d<PAGED, BF>(a, c[0], i, h, step, row_bytes, lane);
+    if (SYNC) next_rows_in_step<NC>(a, c, h, row_bytes, pg, bi, lane);
+    ph_d<PAGED, BF, ADV>(a, c[0], i, h, step, row_bytes, lane);
     ph_a<NC>(c[0], tabs, lane, it);
     CG_SLOT;
     ph_c(c[1]);
@@ -1550,7 +1600,7 @@ __device__ __forceinline__ void chain_pipe(const DecodeArgs& a, Chain* c, int i0
     }
     ph_b(c[0], tabs);
     CG_SLOT;
-    ph_d<PAGED, BF>(a, c[1], i, h, step, row_bytes, lane);
+    ph_d<PAGED, BF, ADV>(a, c[1], i, h, step, row_bytes, lane);
     ph_a<NC>(c[1], tabs, lane, it);
     CG_SLOT;
     if (NC == 3) {
@@ -1562,25 +1612,29 @@ __device__ __forceinline__ void chain_pipe(const DecodeArgs& a, Chain* c, int i0
     ph_b(c[1], tabs);
     CG_SLOT;
     if (NC == 3) {
-      ph_d<PAGED, BF>(a, c[2], i, h, step, row_bytes, lane);
+      ph_d<PAGED, BF, ADV>(a, c[2], i, h, step, row_bytes, lane);
       ph_a<NC>(c[2], tabs, lane, it);
       CG_SLOT;
     }
   }
   // epilogue: finish token i1 - 1
-  ph_d<PAGED, BF>(a, c[0], i1 - 1, h, step, row_bytes, lane);
+  if (SYNC) next_rows_in_step<NC>(a, c, h, row_bytes, pg, bi, lane);
+  ph_d<PAGED, BF, ADV>(a, c[0], i1 - 1, h, step, row_bytes, lane);
   ph_c(c[1]);
   if (NC == 3) ph_b(c[2], tabs);
-  ph_d<PAGED, BF>(a, c[1], i1 - 1, h, step, row_bytes, lane);
+  ph_d<PAGED, BF, ADV>(a, c[1], i1 - 1, h, step, row_bytes, lane);
   if (NC == 3) {
     ph_c(c[2]);
-    ph_d<PAGED, BF>(a, c[2], i1 - 1, h, step, row_bytes, lane);
+    ph_d<PAGED, BF, ADV>(a, c[2], i1 - 1, h, step, row_bytes, lane);
   }
   // the last prefetches may still be in flight into registers the compiler
   // considers free from here on
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-  for (int k = 0; k < NC; ++k) c[k].p = c[k].pb >> 1;
+  for (int k = 0; k < NC; ++k) {
+    c[k].p = c[k].pb >> 1;
+    if (SYNC) c[k].pg_left = pg;
+  }
 }
 
 // NC chains decoded together for their common length, then the longer ones
@@ -1594,7 +1648,15 @@ __device__ __forceinline__ void run_chains(const DecodeArgs& a, Chain* c, const 
   if constexpr (NC == 1) {
     chain_steps<PAGED, 1, BF>(a, c, 1, nmin, tabs, h, step, lane);
   } else {
-    if (nmin > 1) chain_pipe<PAGED, NC, BF>(a, c, 1, nmin, tabs, left, h, step, lane);
+    if (nmin > 1) {
+      bool same_pages = PAGED;
+#pragma unroll
+      for (int k = 1; k < NC; ++k) same_pages = same_pages && c[k].pg_left == c[0].pg_left;
+      if (same_pages)
+        chain_pipe<PAGED, NC, BF, PAGED>(a, c, 1, nmin, tabs, left, h, step, lane);
+      else
+        chain_pipe<PAGED, NC, BF, false>(a, c, 1, nmin, tabs, left, h, step, lane);
+    }
   }
   if constexpr (NC > 1) {
 #pragma unroll
