@@ -1169,10 +1169,10 @@ struct Chain {
   uint32_t doff;               // byte offset of the current output row in dst
   uint32_t pref;               // per lane: the next 128-word block, one dword each
   uint32_t x, q;               // per lane: rANS state, token value mod 2^16
-  int64_t t0;
+  int t0;                      // first token (tokens < 2^26: the host's shape limits)
   int n;
   uint32_t bt0, bt1;           // paged: byte offsets of the pages of blocks bt_base + lane, + 64
-  int64_t bt_base;
+  int bt_base;
   uint32_t pg_left;            // paged: tokens left in the current page after the last stored one
   bool ok;
   // values carried between the phases of one token (pipelined loop)
@@ -1194,7 +1194,7 @@ struct GroupRef {
 
 // Byte offset in the (layer, K|V) slab of the pool of the first row of head
 // h in the page of block-table entry i (0 past the chain's last block).
-__device__ __forceinline__ uint32_t page_offset(const DecodeArgs& a, int64_t i, int64_t last, int h,
+__device__ __forceinline__ uint32_t page_offset(const DecodeArgs& a, int i, int last, int h,
                                                 uint32_t row_bytes) {
   if (i > last) return 0u;
   const uint32_t blk = (uint32_t)a.block_table[i];
@@ -1204,7 +1204,7 @@ __device__ __forceinline__ uint32_t page_offset(const DecodeArgs& a, int64_t i, 
 // The chain's window of 128 block-table entries from bt_base on, as page
 // offsets in two registers (entry bt_base + lane, + 64).
 __device__ __forceinline__ void load_pages(const DecodeArgs& a, Chain& c, int h, uint32_t row_bytes, int lane) {
-  const int64_t last = (c.t0 + c.n - 1) >> 4;
+  const int last = (c.t0 + c.n - 1) >> 4;
   c.bt0 = page_offset(a, c.bt_base + lane, last, h, row_bytes);
   c.bt1 = page_offset(a, c.bt_base + 64 + lane, last, h, row_bytes);
 }
@@ -1215,10 +1215,10 @@ __device__ __forceinline__ uint32_t page_in_window(const Chain& c, uint32_t bi) 
 }
 
 template <bool PAGED>
-__device__ __forceinline__ uint32_t row_offset(const DecodeArgs& a, Chain& c, int64_t t, int h,
+__device__ __forceinline__ uint32_t row_offset(const DecodeArgs& a, Chain& c, int t, int h,
                                                uint32_t row_bytes, int lane) {
   if (!PAGED) return (uint32_t)(t - c.t0) * row_bytes;
-  const int64_t b = (t >> 4) - c.bt_base;
+  const int b = (t >> 4) - c.bt_base;
   if (__builtin_expect(b >= 128, 0)) {  // next window of 128 block-table entries
     c.bt_base += 128;
     load_pages(a, c, h, row_bytes, lane);
@@ -1279,7 +1279,7 @@ __device__ __forceinline__ void chain_open(const DecodeArgs& a, Chain& c, const 
   c.src = make_rsrc(gr.rec + gr.ds + o0, (uint32_t)(o1 - o0));
   c.ring = ring;
   c.nw = nw;
-  c.t0 = gr.t0;
+  c.t0 = (int)gr.t0;
   c.n = gr.n;
   {
     const uint32_t v0 = stream_load(c, 0, lane), v1 = stream_load(c, kRingBlock, lane);
@@ -1300,10 +1300,10 @@ __device__ __forceinline__ void chain_open(const DecodeArgs& a, Chain& c, const 
   } else {
     const uint16_t* p0 = a.pool + ((size_t)gr.l * 2 + kv) * (size_t)a.num_blocks * s.H * 16 * s.D + col;
     c.dst = make_rsrc(p0, (uint32_t)((uint64_t)a.num_blocks * s.H * 16 * row_bytes));
-    c.bt_base = gr.t0 >> 4;
+    c.bt_base = c.t0 >> 4;
     load_pages(a, c, h, row_bytes, lane);
   }
-  c.doff = row_offset<PAGED>(a, c, gr.t0, h, row_bytes, lane);
+  c.doff = row_offset<PAGED>(a, c, c.t0, h, row_bytes, lane);
   c.pg_left = 15u - (uint32_t)(gr.t0 & 15);
   __builtin_amdgcn_raw_buffer_store_b16(dequantize_low16<BF>(c.q, step), c.dst, 2u * lane, c.doff, 0);
 }
