@@ -389,7 +389,7 @@ __device__ __forceinline__ void hist_range(__amdgpu_buffer_rsrc_t xr, uint32_t r
                                            int t_end, int C, float step, float rcp, uint32_t* hist,
                                            int* left, int wave, int lane, uint32_t& sat,
                                            uint32_t& nan_) {
-  const uint32_t lane2 = 2u * lane;
+  const uint32_t lane2 = 2u * lane, lane4 = 4u * lane;
   uint32_t* hl = hist + lane;
   int32_t prev = 0;
   int pos = t_begin % C;  // position of the next token inside its chunk
@@ -407,8 +407,16 @@ __device__ __forceinline__ void hist_range(__amdgpu_buffer_rsrc_t xr, uint32_t r
       nan_ += n0;
     }
     const uint32_t r = sym_raw(q, prev);
-    const uint32_t sym = pos != 0 ? (r < 255u ? r : 255u) : 256u;  // row 256: chunk heads
-    atomicAdd(hl + sym * 64, 1u);
+    // byte offset of row min(r, 255), column lane, in one shift-or (the
+    // compiler splits it in two)
+    uint32_t off;
+    asm("v_lshl_or_b32 %0, %1, 8, %2" : "=v"(off) : "v"(r < 255u ? r : 255u), "v"(lane4));
+    uint32_t* cell = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(hist) + off);
+    atomicAdd(cell, 1u);
+    if (__builtin_expect(pos == 0, 0)) {  // a chunk head has no symbol: row 256 counts it instead
+      atomicSub(cell, 1u);
+      atomicAdd(hl + 256 * 64, 1u);
+    }
     prev = q;
     pos = (pos + 1 == C) ? 0 : pos + 1;
   };
