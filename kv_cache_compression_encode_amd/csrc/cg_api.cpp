@@ -457,17 +457,20 @@ static cg_status decode_common(const cg_shape* shape, int32_t n_levels, const cg
     a->n_groups[k] = levels[k].n_groups;
     if (levels[k].n_groups > g_max) g_max = levels[k].n_groups;
   }
-  if ((uint64_t)n_refs * g_max * 2 * s.H * s.S >= (1ull << 31)) return CG_ERR_UNSUPPORTED;
+  if ((uint64_t)n_refs * g_max * 2 * s.H * s.S * n_levels >= (1ull << 31)) return CG_ERR_UNSUPPORTED;
   a->s = s;
   a->refs = refs_dev;
   a->n_refs = n_refs;
-  if (n_levels == 1) {
-    plan_decode(s, levels[0], n_refs, a);
-  } else {
-    a->refs_per_block = 1;
-    a->split = 0;
-    a->refs_per_block2 = 1;
-  }
+  // several levels: records of a workgroup must share a table set, and which
+  // set each record names is on the device, so every block of records is
+  // launched once per set and decodes its records of that set; the blocks
+  // are sized for the level with the most layers per group (runs of records
+  // of one level fill them)
+  int widest = 0;
+  for (int k = 1; k < n_levels; ++k)
+    if (max_layers_per_group(s, levels[k]) > max_layers_per_group(s, levels[widest])) widest = k;
+  plan_decode(s, levels[widest], n_refs, a);
+  a->per_level = n_levels > 1;
   a->n_tables = n_levels;
   a->g_max = g_max;
   a->status = status_dev;
@@ -639,6 +642,7 @@ cg_status cg_stream_decode_paged(const cg_shape* shape, int32_t n_levels, const 
       a.refs_per_block = 1;
       a.split = 0;
       a.refs_per_block2 = 1;
+      a.per_level = 0;  // one record: its own set
       e = launch_decode(a, true, stream);
     }
     if (e == hipSuccess) e = hipEventRecord(consumed[slot], stream);

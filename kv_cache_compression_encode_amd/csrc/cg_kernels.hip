@@ -1690,8 +1690,14 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
   const int kv = (int)(bid % 2);
   bid /= 2;
   const int g = (int)(bid % a.g_max);
-  const int64_t rb = bid / a.g_max;
+  int64_t rb = bid / a.g_max;
   const int64_t nb1 = a.split / a.refs_per_block;
+  int lvl = 0;  // several levels: the table set of this copy of the blocks
+  if (a.per_level) {
+    const int64_t rblocks = nb1 + (a.n_refs - a.split + a.refs_per_block2 - 1) / a.refs_per_block2;
+    lvl = (int)(rb / rblocks);
+    rb -= lvl * rblocks;
+  }
   int64_t r_begin, r_end;
   if (rb < nb1) {
     r_begin = rb * a.refs_per_block;
@@ -1700,10 +1706,11 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
     r_begin = a.split + (rb - nb1) * a.refs_per_block2;
     r_end = r_begin + a.refs_per_block2 < a.n_refs ? r_begin + a.refs_per_block2 : a.n_refs;
   }
-  const bool first_block = (g == 0 && kv == 0 && h == 0 && j == 0);
+  const bool first_block = (g == 0 && kv == 0 && h == 0 && j == 0 && lvl == 0);
 
-  // all records of a workgroup use the first one's table set
-  const int ti = uni(a.refs[r_begin].table);
+  // the workgroup's table set: its copy's (several levels), else its first
+  // record's, which the other records must share
+  const int ti = a.per_level ? lvl : uni(a.refs[r_begin].table);
   if (ti < 0 || ti >= a.n_tables) {
     if (tid == 0 && first_block) set_status(a.status, CG_ERR_INVALID_ARG);
     return;
@@ -1728,8 +1735,9 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
     const uint8_t* rec = uni(a.refs[r].record);
     const uint64_t ref_bytes = uni(a.refs[r].bytes);
     const int rti = uni(a.refs[r].table);
-    if (rti != ti) {
-      if (tid == 0 && first_block) set_status(a.status, CG_ERR_INVALID_ARG);
+    if (rti != ti) {  // another copy decodes it, or no table set has that index
+      if (tid == 0 && first_block && (!a.per_level || rti < 0 || rti >= a.n_tables))
+        set_status(a.status, CG_ERR_INVALID_ARG);
       continue;
     }
     if (ref_bytes < ds_expect || (reinterpret_cast<uintptr_t>(rec) & 15)) {
@@ -2189,7 +2197,7 @@ hipError_t launch_attend_reduce(const AttendArgs& a, hipStream_t st) {
 hipError_t launch_decode(const DecodeArgs& a, bool paged, hipStream_t st) {
   const uint64_t rblocks = (uint64_t)(a.split / a.refs_per_block) +
                            (uint64_t)(a.n_refs - a.split + a.refs_per_block2 - 1) / a.refs_per_block2;
-  const uint64_t blocks = rblocks * a.g_max * 2 * a.s.H * a.s.S;
+  const uint64_t blocks = rblocks * (a.per_level ? a.n_tables : 1) * a.g_max * 2 * a.s.H * a.s.S;
   const bool bf = a.s.dt == kDtypeBf16;
   if (paged && bf)
     hipLaunchKernelGGL((k_decode<true, true>), dim3((unsigned)blocks), dim3(kDecThreads), 0, st, a);

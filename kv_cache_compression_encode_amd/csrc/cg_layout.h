@@ -215,6 +215,10 @@ struct DecodeArgs {
   int32_t refs_per_block;
   int32_t split;
   int32_t refs_per_block2;
+  // per_level: the grid holds one copy of these blocks per table set, and a
+  // block decodes only the records of its copy's set (records of several
+  // levels in any order); otherwise a block's set is its first record's
+  int32_t per_level;
   int32_t n_tables;
   int32_t g_max;
   const uint8_t* tables[kMaxLevels];
