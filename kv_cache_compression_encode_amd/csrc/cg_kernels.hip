@@ -1636,8 +1636,11 @@ __device__ __forceinline__ void chain_pipe(const DecodeArgs& a, Chain* c, int i0
     ph_d<PAGED, BF, ADV>(a, c[2], i1 - 1, h, step, row_bytes, lane);
   }
   // the last prefetches may still be in flight into registers the compiler
-  // considers free from here on
+  // considers free from here on; the empty uses keep those registers
+  // reserved (not reassigned to other values) until the wait
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int k = 0; k < NC; ++k) asm volatile("" ::"v"(c[k].pref));
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
     c[k].p = c[k].pb >> 1;
