@@ -215,6 +215,21 @@ cg_status cg_decode_paged(const cg_shape* shape, int32_t n_levels, const cg_leve
                           const int32_t* block_table_dev, int32_t* status_dev,
                           const cg_profile* prof, hipStream_t stream);
 
+/* The dispatch plan cg_decode and cg_decode_paged launch for n_refs records
+ * of these levels (host only, no device work). A decode workgroup holds the
+ * decoder tables of one table set (one layer group, K|V, head and 64-dim
+ * slice) and decodes that set's groups of a block of records; records
+ * [0, split) go in blocks of records_per_block, the rest in blocks of
+ * records_per_block2, and a block's groups are dealt to 16 wavefronts that
+ * decode up to three of them as interleaved chains. The plan minimises a
+ * simulated dispatch over the current device's compute units (256 when no
+ * device is visible). Writes out_host[3] = {records_per_block, split,
+ * records_per_block2}. Returns CG_ERR_INVALID_ARG for n_refs < 1, a null
+ * pointer or n_levels outside 1..8, and the shape and level checks of
+ * cg_decode. */
+cg_status cg_decode_plan(const cg_shape* shape, int32_t n_levels, const cg_level* levels, int32_t n_refs,
+                         int32_t* out_host);
+
 /* Streaming fill of a paged cache ("CacheGen实战" 2.3: a receive stage, a
  * parallel GPU decode stage and a fill stage run as a pipeline). Records
  * [0, n_records) lie in host memory at records_host + offsets_host[k]

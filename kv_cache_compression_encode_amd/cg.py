@@ -138,6 +138,7 @@ def lib():
         "cg_make_refs": (i32, [P, P, i32, i32, P, P]),
         "cg_decode": (i32, [sp, i32, lp, P, P, i32, P, P, pp, P]),
         "cg_decode_paged": (i32, [sp, i32, lp, P, P, i32, P, i64, P, P, pp, P]),
+        "cg_decode_plan": (i32, [sp, i32, lp, i32, P]),
         "cg_copy": (i32, [P, P, u64, P]),
         "cg_select_level": (i32, [ctypes.c_double]),
         "cg_recency_levels": (i32, [i64, i64, i64, P]),
@@ -156,7 +157,7 @@ def lib():
 EXPORTS = ("cg_version", "cg_status_string", "cg_tables_bytes", "cg_tables_format_bytes",
            "cg_build_workspace_bytes", "cg_build_tables", "cg_encode_bound",
            "cg_encode_workspace_bytes", "cg_encode", "cg_make_refs", "cg_decode",
-           "cg_decode_paged", "cg_stream_decode_paged", "cg_copy", "cg_select_level",
+           "cg_decode_paged", "cg_decode_plan", "cg_stream_decode_paged", "cg_copy", "cg_select_level",
            "cg_recency_levels", "cg_attend_workspace_bytes", "cg_attend_paged")
 
 
@@ -259,6 +260,15 @@ def cg_decode_paged(shp, levels, tables, refs, n_refs, pool, num_blocks, block_t
                                _ptr(pool), int(num_blocks), _ptr(block_table), _ptr(status),
                                _prof(prof), _stream(stream))
     _check("cg_decode_paged", rc)
+
+
+def cg_decode_plan(shp, levels, n_refs):
+    """(records_per_block, split, records_per_block2) of the decode dispatch."""
+    arr = (cg_level * len(levels))(*[lv.c for lv in levels])
+    out = np.zeros(3, dtype=np.int32)
+    _check("cg_decode_plan", lib().cg_decode_plan(ctypes.byref(shp), len(levels), arr, int(n_refs),
+                                                  out.ctypes.data))
+    return int(out[0]), int(out[1]), int(out[2])
 
 
 def cg_attend_workspace_bytes(shp, q_heads, n_tokens) -> int:

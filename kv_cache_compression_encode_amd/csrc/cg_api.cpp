@@ -477,6 +477,25 @@ static cg_status decode_common(const cg_shape* shape, int32_t n_levels, const cg
   return CG_OK;
 }
 
+cg_status cg_decode_plan(const cg_shape* shape, int32_t n_levels, const cg_level* levels, int32_t n_refs,
+                         int32_t* out_host) {
+  Shape s;
+  cg_status rc = check_shape(shape, &s);
+  if (rc != CG_OK) return rc;
+  if (!levels || !out_host || n_levels < 1 || n_levels > kMaxLevels || n_refs < 1) return CG_ERR_INVALID_ARG;
+  for (int k = 0; k < n_levels; ++k)
+    if ((rc = check_level(&levels[k], s)) != CG_OK) return rc;
+  int widest = 0;  // as in decode_common
+  for (int k = 1; k < n_levels; ++k)
+    if (max_layers_per_group(s, levels[k]) > max_layers_per_group(s, levels[widest])) widest = k;
+  DecodeArgs a;
+  plan_decode(s, levels[widest], n_refs, &a);
+  out_host[0] = a.refs_per_block;
+  out_host[1] = a.split;
+  out_host[2] = a.refs_per_block2;
+  return CG_OK;
+}
+
 cg_status cg_decode(const cg_shape* shape, int32_t n_levels, const cg_level* levels,
                     const void* const* tables_dev, const cg_chunk_ref* refs_dev, int32_t n_refs,
                     uint16_t* y_dev, int32_t* status_dev, const cg_profile* prof,
