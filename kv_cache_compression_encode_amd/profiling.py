@@ -8,7 +8,11 @@
   plain copy kernel (k_copy) moving a known number of bytes. Written as JSON
   (read by bench.py) and as markdown.
 
-Both record the source hash of the kernels they describe; bench.py reports
+- ``stall``: where the waves' time goes per kernel (waiting at s_waitcnt,
+  issuing scalar ALU, LDS or other instructions) from two SQ counter passes
+  over the same workload, as markdown.
+
+All record the source hash of the kernels they describe; bench.py reports
 the traffic only while the kernel sources still have that hash.
 """
 from __future__ import annotations
@@ -113,6 +117,29 @@ def sq(sq_dir: str, trace_dir: str):
     return out
 
 
+STALL_A = ("SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_ANY",
+           "SQ_ACTIVE_INST_SCA", "SQ_ACTIVE_INST_MISC")
+STALL_B = ("SQ_INSTS_VALU", "SQ_LDS_DATA_FIFO_FULL")
+
+
+def stall(a_dir: str, b_dir: str):
+    """Per kernel: fractions of the waves' lifetimes (SQ_WAVE_CYCLES) spent
+    waiting at s_waitcnt, waiting to issue LDS instructions, issuing any,
+    scalar-ALU or other sequencer instructions (mean per dispatch)."""
+    per = {c: counter_per_kernel(a_dir, c) for c in STALL_A}
+    per.update({c: counter_per_kernel(b_dir, c) for c in STALL_B})
+    out = {}
+    for k, wc in per["SQ_WAVE_CYCLES"].items():
+        if not wc or k == "k_copy":
+            continue
+        out[k] = {"wave_cycles": 4 * wc, "wait": per["SQ_WAIT_INST_ANY"][k] / wc,
+                  "wait_lds": per["SQ_WAIT_INST_LDS"][k] / wc, "issue": per["SQ_ACTIVE_INST_ANY"][k] / wc,
+                  "scalar": per["SQ_ACTIVE_INST_SCA"][k] / wc, "misc": per["SQ_ACTIVE_INST_MISC"][k] / wc,
+                  "valu_insts": per["SQ_INSTS_VALU"].get(k, 0.0),
+                  "lds_fifo_full": per["SQ_LDS_DATA_FIFO_FULL"].get(k, 0.0)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -130,6 +157,12 @@ def main():
     t.add_argument("--command", required=True, help="the two commands, ';'-separated")
     t.add_argument("--json", required=True, help="traffic JSON (merged per workload)")
     t.add_argument("--md", required=True)
+    w = sub.add_parser("stall")
+    w.add_argument("--a", required=True, help="output dir of the first stall counter pass")
+    w.add_argument("--b", required=True, help="output dir of the second stall counter pass")
+    w.add_argument("--config", required=True)
+    w.add_argument("--command", required=True, help="the commands, ';'-separated lines")
+    w.add_argument("--md", required=True)
     q = sub.add_parser("sq")
     q.add_argument("--sq", required=True, help="output dir of the SQ counter run")
     q.add_argument("--trace", required=True, help="output dir of a kernel-trace run of the same sources")
@@ -138,6 +171,29 @@ def main():
     q.add_argument("--json", required=True)
     q.add_argument("--md", required=True)
     a = ap.parse_args()
+    if a.cmd == "stall":
+        res = stall(a.a, a.b)
+        with open(a.md, "w") as f:
+            f.write("# Wave stall counters per launch, %s workload (rocprofv3)\n\n" % a.config)
+            f.write("Kernel sources: hash `%s`. SQ_WAVE_CYCLES, SQ_WAIT_INST_ANY and SQ_ACTIVE_INST_* count in "
+                    "units of 4 cycles summed over waves; the fractions are of the waves' lifetimes "
+                    "(SQ_WAVE_CYCLES). Waiting: at an s_waitcnt; LDS issue: waiting to issue an LDS "
+                    "instruction; scalar: issuing scalar ALU; misc: branches and other sequencer "
+                    "instructions. Two counter passes (at most 8 SQ counters each) over the same "
+                    "one-step run.\n\n" % source_hash())
+            f.write("Commands (repository root):\n\n```\n%s\n```\n\n" % a.command.replace(";", "\n"))
+            f.write("| kernel | waves' cycles | waiting (s_waitcnt) | waiting to issue LDS | issuing any | "
+                    "issuing scalar ALU | branches/misc | VALU insts | LDS data FIFO full |\n"
+                    "|---|---|---|---|---|---|---|---|---|\n")
+            for k in ("k_decode", "k_encode", "k_hist", "k_write", "k_decode_paged", "k_attend"):
+                if k not in res:
+                    continue
+                e = res[k]
+                f.write("| %s | %.4g | %.1f %% | %.1f %% | %.1f %% | %.1f %% | %.1f %% | %.4g | %d |\n" % (
+                    k, e["wave_cycles"], 100 * e["wait"], 100 * e["wait_lds"], 100 * e["issue"],
+                    100 * e["scalar"], 100 * e["misc"], e["valu_insts"], e["lds_fifo_full"]))
+        print("wrote", a.md)
+        return
     if a.cmd == "sq":
         res = sq(a.sq, a.trace)
         doc = {}
