@@ -14,15 +14,23 @@ from tests import gpu_util as U
 
 pytestmark = pytest.mark.gpu
 
-L, H, D, T, CC = 16, 8, 128, 600, 40  # 15 chunks: the planner pairs records
+SHAPES = [
+    # L, H, D, T, CC (15 chunks), records per decode workgroup
+    (16, 8, 128, 600, 40, 2),
+    (16, 64, 64, 150, 10, 3),
+]
 LEVELS = [(3, [0] * 16, [0.5]), (4, [0] * 8 + [1] * 8, [0.8, 1.2])]
 
 
-@pytest.fixture(scope="module")
-def two_levels():
+@pytest.fixture(scope="module", params=SHAPES, ids=["2-records", "3-records"])
+def two_levels(request):
     U.need_gpu()
     torch = U.torch
     O = U.O
+    L, H, D, T, CC, rpb = request.param
+    print("shape", request.param, flush=True)
+    levels = [U.C.Level(lid, lg, st) for lid, lg, st in LEVELS]
+    assert U.C.cg_decode_plan(U.C.shape(L, H, D, T, CC), levels, -(-T // CC))[0] == rpb
     X = synth.random_kv(L, H, D, T, 81)
     shp = U.C.shape(L, H, D, T, CC)
     cd = U.codec.Codec(shp)
@@ -42,11 +50,12 @@ def two_levels():
         assert np.array_equal(offs.cpu().numpy().astype(np.uint64), ooffs)
         oracle.append((blob, data, ooffs))
     torch.cuda.synchronize()
-    return cd, gl, tabs, outs, oshp, oracle
+    return cd, gl, tabs, outs, oshp, oracle, (L, H, D, T, CC)
 
 
-def expected(oshp, oracle, mix):
+def expected(oshp, oracle, mix, dims):
     O = U.O
+    L, H, D, T, CC = dims
     ref = np.zeros((L, 2, H, T, D), dtype=np.uint16)
     for c, m in enumerate(mix):
         blob, data, offs = oracle[int(m)]
@@ -56,7 +65,8 @@ def expected(oshp, oracle, mix):
 
 @pytest.mark.parametrize("pattern", ["runs", "alternating", "random-reversed"])
 def test_level_mix_in_shared_blocks(two_levels, pattern):
-    cd, gl, tabs, outs, oshp, oracle = two_levels
+    cd, gl, tabs, outs, oshp, oracle, dims = two_levels
+    T, CC = dims[3], dims[4]
     n = -(-T // CC)
     if pattern == "runs":
         mix = np.array([0] * 7 + [1] * 8)
@@ -69,11 +79,11 @@ def test_level_mix_in_shared_blocks(two_levels, pattern):
     refs, nr = cd.make_refs(parts)
     y = cd.decode(gl, tabs, refs, nr)
     assert cd.read_status() == 0
-    assert np.array_equal(y.cpu().numpy().view(np.uint16), expected(oshp, oracle, mix))
+    assert np.array_equal(y.cpu().numpy().view(np.uint16), expected(oshp, oracle, mix, dims))
 
 
 def test_table_index_out_of_range_with_levels(two_levels):
-    cd, gl, tabs, outs, oshp, oracle = two_levels
+    cd, gl, tabs, outs, oshp, oracle, _ = two_levels
     out, offs = outs[0]
     parts = [(out, offs, [0, 1], 0), (out, offs, [2], 2), (out, offs, [3], 0)]  # table 2: only 2 passed
     refs, nr = cd.make_refs(parts)
