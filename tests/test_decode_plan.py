@@ -19,7 +19,7 @@ def plan(L, H, D, T, Cc, groups):
 
 
 def test_few_workgroups_take_one_record_each():
-    # 2 table sets x 4 records fit the chip in one round: the shortest
+    # 2 table sets x 4 records all run at once on the 256 compute units: the shortest
     # workgroup (one record, one chain per wavefront) gives the shortest run
     assert plan(16, 1, 64, 1024, 256, 1) == (1, 0, 1)
     from kv_cache_compression_encode_amd import cg as C
