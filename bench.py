@@ -82,6 +82,8 @@ def main():
                     help="robust tables from the first quarter of the tokens")
     ap.add_argument("--attend", action="store_true",
                     help="time decode into a paged pool + attention over it")
+    ap.add_argument("--level-mix", action="store_true",
+                    help="time a decode of chunk records of three quality levels mixed per chunk")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed steps, one library copy of this many bytes (the calibration "
                          "launch for the FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -150,6 +152,8 @@ def main():
 
     if args.attend:
         return run_attend(args, cfg, lvd, cd, x, shp, lv, tables, out, offs, refs, nch, stream)
+    if args.level_mix:
+        return run_level_mix(args, cfg, cd, x, shp, stream)
 
     for _ in range(args.warmup):
         step()
@@ -301,6 +305,116 @@ def main():
     if not args.no_cpu_baseline:
         xb = x[:1].cpu().view(torch.int16).numpy().view(np.uint16)
         res["cpu_baseline"] = cpu_baseline(cfg, xb, args.cpu_seconds, dt, flags)
+    print(json.dumps(res), flush=True)
+
+
+def run_level_mix(args, cfg, cd, x, shp, stream):
+    """Every chunk encoded at the three quality levels ("CacheGen实战" 2.1 and
+    3.1: high 0.3/0.8/1.2, balanced 0.5/1.0/1.5, fast 0.8/1.5/2.0 over thirds
+    of the layers), then one cg_decode of the records of a per-chunk level mix
+    drawn from the seed. Step = that decode with the references in chunk
+    order (levels interleaved); the same records referenced in runs of one
+    level are timed beside it."""
+    import numpy as np
+    import torch
+
+    from kv_cache_compression_encode_amd import cg as C
+    from kv_cache_compression_encode_amd import codec, synth
+
+    dev = x.device
+    nch = codec.n_chunks(shp)
+    presets = synth.CONFIGS["long"].levels  # the same 48-layer groups
+    assert len(presets[0].layer_group) == cfg.layers
+    lvs = [codec.level_of(p) for p in presets]
+    tabs, outs, ratios = [], [], []
+    for lv in lvs:
+        t = cd.build_tables(x, lv)
+        out, offs = cd.encode(x, lv, t)
+        tabs.append(t)
+        outs.append((out, offs))
+    torch.cuda.synchronize()
+    assert cd.read_status() == 0
+    fp16_bytes = 2 * x.numel()
+    for out, offs in outs:
+        ratios.append(round(fp16_bytes / int(offs[-1].item()), 3))
+    mix = np.random.default_rng([0, cfg.config_id, 999]).integers(0, len(lvs), nch)
+    order_mixed = list(range(nch))
+    order_runs = sorted(range(nch), key=lambda c: (int(mix[c]), c))
+    refs = {}
+    for name, order in (("mixed", order_mixed), ("runs", order_runs)):
+        refs[name] = cd.make_refs([(outs[int(mix[c])][0], outs[int(mix[c])][1], [c], int(mix[c])) for c in order])
+    y = torch.empty_like(x)
+    comp = sum(int((outs[int(mix[c])][1][c + 1] - outs[int(mix[c])][1][c]).item()) for c in range(nch))
+
+    def timed(name):
+        r, n = refs[name]
+        for _ in range(args.warmup):
+            cd.decode(lvs, tabs, r, n, y=y)
+        torch.cuda.synchronize()
+        assert cd.read_status() == 0
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        kt = [C.KernelTimer() for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        ev[0].record(stream)
+        for k in range(args.steps):
+            cd.decode(lvs, tabs, r, n, y=y, prof=kt[k])
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        assert cd.read_status() == 0
+        call = float(np.mean([ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]))
+        return wall, call, float(np.mean([t.elapsed_ms() for t in kt]))
+
+    wall_r, call_r, kern_r = timed("runs")
+    wall, call, kern = timed("mixed")
+    # correctness of this run: sampled (layer, K|V, head) slices against
+    # numpy's dequant(quant(x)) with each chunk's own level
+    rng = np.random.default_rng(2)
+    for _ in range(4):
+        l, kv, h = int(rng.integers(cfg.layers)), int(rng.integers(2)), int(rng.integers(cfg.kv_heads))
+        xs = x[l, kv, h].cpu().to(torch.float64).numpy()
+        got = y[l, kv, h].cpu().view(torch.int16).numpy().view(np.uint16)
+        for c in range(nch):
+            p = presets[int(mix[c])]
+            st = np.float32(p.steps[p.layer_group[l]])
+            rows = slice(c * cfg.chunk_tokens, min((c + 1) * cfg.chunk_tokens, cfg.tokens))
+            with np.errstate(all="ignore"):
+                q = np.clip(np.rint((xs[rows] / np.float64(st)).astype(np.float32)), -32768, 32767)
+                q = np.nan_to_num(q).astype(np.int32)
+                ref = torch.from_numpy(q.astype(np.float32) * st).to(x.dtype).view(torch.int16).numpy().view(np.uint16)
+            assert np.array_equal(got[rows], ref), (l, kv, h, c)
+    n_tables = sum(2 * lv.n_groups * cfg.kv_heads * cfg.head_dim for lv in lvs)
+    dec_bytes = fp16_bytes + comp + n_tables * 2048
+    gbps = dec_bytes / (kern / 1e3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(fp16_bytes / (wall / args.steps) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "%s data; fp32 dequantize, u32 rANS" % args.dtype,
+        "data": "synthetic",
+        "config": {"workload": "%s level mix: %d layers x %d KV heads x %d dim x %d tokens, chunk %d, each "
+                               "chunk encoded at high/balanced/fast, decoded at a seeded per-chunk mix "
+                               "(%s)" % (cfg.name, cfg.layers, cfg.kv_heads, cfg.head_dim, cfg.tokens,
+                                         cfg.chunk_tokens, "".join("hbf"[int(m)] for m in mix)),
+                   "fp16_bytes": fp16_bytes, "chunks": nch},
+        "decode_ms": round(call, 4),
+        "decode_GBps": round(fp16_bytes / (call / 1e3) / 1e9, 1),
+        "decode_runs_ms": round(call_r, 4),
+        "decode_runs_GBps": round(fp16_bytes / (call_r / 1e3) / 1e9, 1),
+        "ratio_per_level": dict(zip(("high", "balanced", "fast"), ratios)),
+        "compressed_bytes_mixed": comp,
+        "roofline": {"kernel": "k_decode", "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes": int(dec_bytes), "avg_ms": round(kern, 4)},
+        "kernel_ms": {"k_decode_mixed": round(kern, 4), "k_decode_runs": round(kern_r, 4)},
+    }
     print(json.dumps(res), flush=True)
 
 

@@ -189,10 +189,10 @@ cg_status cg_make_refs(const uint8_t* base_dev, const uint64_t* offsets_dev, int
  * tensor y_dev ("CacheGen实战" 2.3: parallel GPU decode). Record i is read
  * with tables_dev[refs[i].table], which must have been built for
  * levels[refs[i].table]; records of different levels may be mixed (section
- * 2.1), in any order (a record's header names its chunk); runs of records
- * of one level decode fastest, as up to three consecutive references share
- * a workgroup when they name the same table set. Only the token ranges of
- * the given chunks are written.
+ * 2.1), in any order (a record's header names its chunk). With one level,
+ * up to three consecutive references share a workgroup; with several, each
+ * table set's records share workgroups in reference order however the
+ * levels interleave. Only the token ranges of the given chunks are written.
  * n_levels <= 8. levels and tables_dev are host arrays; tables_dev[k] is a
  * device pointer. Data errors: CG_ERR_CORRUPT (bad record header, group
  * offsets, final rANS state or word count), CG_ERR_INVALID_ARG (table index

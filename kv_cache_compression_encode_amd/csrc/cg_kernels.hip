@@ -1678,6 +1678,38 @@ __device__ __forceinline__ void run_chains(const DecodeArgs& a, Chain* c, const 
   for (int k = 0; k < NC; ++k) chain_close(a, c[k], lane);
 }
 
+// Several levels: the positions of the references that name table set lvl
+// and whose rank among those references lies in [k0, k1), in reference order
+// (at most kMaxRefsPerBlock), so a workgroup's records share its set however
+// the levels of neighbouring references mix. Each wavefront scans the table
+// indices 64 at a time (the results are wave-uniform). With all_refs the
+// scan covers every reference; *bad reports one that names no table set.
+__device__ __forceinline__ int refs_of_set(const DecodeArgs& a, int lvl, int64_t k0, int64_t k1, int64_t* sel,
+                                           bool all_refs, bool* bad, int lane) {
+  int found = 0;
+  int64_t rank = 0;
+  bool b = false;
+  for (int64_t base = 0; base < a.n_refs && (rank < k1 || all_refs); base += 64) {
+    const int64_t r = base + lane;
+    const int t = r < a.n_refs ? a.refs[r].table : -1;
+    b |= __ballot(r < a.n_refs && (t < 0 || t >= a.n_tables)) != 0;
+    uint64_t m = __ballot(t == lvl);
+    const int64_t cnt = __popcll(m);
+    if (rank + cnt <= k0 || rank >= k1) {
+      rank += cnt;
+      continue;
+    }
+    while (m != 0 && rank < k1) {
+      const int bit = __builtin_ctzll(m);
+      m &= m - 1;
+      if (rank >= k0 && found < kMaxRefsPerBlock) sel[found++] = base + bit;
+      ++rank;
+    }
+  }
+  *bad = b;
+  return found;
+}
+
 template <bool PAGED, bool BF>
 __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
   __shared__ uint32_t tabs[kDecDwords * 64];
@@ -1730,11 +1762,25 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
   const uint64_t ds_expect = rec_data_start(gpc);
   const int64_t nch = n_chunks(s.T, s.C);
 
+  // the workgroup's references: its block's (one level), else those of its
+  // table set with ranks in the block's range (several levels)
+  int64_t sel[kMaxRefsPerBlock];
+  int nsel = 0;
+  if (a.per_level) {
+    bool bad_ref = false;
+    const bool reporter = first_block && rb == 0;
+    nsel = refs_of_set(a, lvl, r_begin, r_end, sel, reporter, &bad_ref, lane);
+    if (bad_ref && reporter && tid == 0) set_status(a.status, CG_ERR_INVALID_ARG);
+  } else {
+    for (int64_t r = r_begin; r < r_end && nsel < kMaxRefsPerBlock; ++r) sel[nsel++] = r;
+  }
+
   // record headers of this workgroup (at most kMaxRefsPerBlock = 3)
   GroupRef rr0, rr1, rr2;
   rr0.l = rr1.l = rr2.l = 0;
   int nrec = 0;
-  for (int64_t r = r_begin; r < r_end && nrec < kMaxRefsPerBlock; ++r) {
+  for (int k = 0; k < nsel; ++k) {
+    const int64_t r = sel[k];
     const uint8_t* rec = uni(a.refs[r].record);
     const uint64_t ref_bytes = uni(a.refs[r].bytes);
     const int rti = uni(a.refs[r].table);
