@@ -8,6 +8,7 @@
 #include <cstring>
 #include <algorithm>
 #include <functional>
+#include <utility>
 #include <vector>
 
 #include "cg_layout.h"
@@ -115,42 +116,58 @@ struct BlockPlan {
   int r1 = 1, split = 0, r2 = 1;
 };
 
+// Greedy dispatch of equal-cost workgroups: each goes to the compute unit
+// that frees first. The units' finish times are kept as (time, count) groups
+// in ascending order, so a run of workgroups costs a few group moves instead
+// of one heap operation per workgroup (the multiset of finish times, and so
+// the span, is what the per-workgroup simulation gives).
+struct Dispatch {
+  std::vector<std::pair<int64_t, int64_t>> g;  // finish time -> units, ascending
+  explicit Dispatch(int64_t cus) : g{{0, cus}} {}
+  void add(int64_t t, int64_t c) {
+    auto it = g.begin();
+    while (it != g.end() && it->first < t) ++it;
+    if (it != g.end() && it->first == t)
+      it->second += c;
+    else
+      g.insert(it, {t, c});
+  }
+  void run(int64_t jobs, int64_t t) {
+    while (jobs > 0) {
+      const int64_t t0 = g.front().first, c = g.front().second;
+      const int64_t k = c < jobs ? c : jobs;
+      if (k == c)
+        g.erase(g.begin());
+      else
+        g.front().second -= k;
+      add(t0 + t, k);
+      jobs -= k;
+    }
+  }
+  int64_t span() const { return g.back().first; }
+};
+
 template <class Cost>
 static BlockPlan plan_blocks(int64_t n_rec, int64_t sets, int max_r, int64_t last, Cost cost) {
   const int cus = compute_units();
   BlockPlan best;
   int64_t best_span = INT64_MAX;
-  std::vector<int64_t> heap;
   for (int r1 = 1; r1 <= max_r && r1 <= n_rec; ++r1) {
     for (int r2 = 1; r2 <= r1; ++r2) {
       for (int64_t split = 0; split <= n_rec; split += r1) {
         if (split == n_rec && r2 != 1) continue;  // no second class
         const int64_t n1 = split / r1, n2 = (n_rec - split + r2 - 1) / r2;
         const int64_t rem = (n_rec - split) % r2;
-        int64_t span;
-        if ((n1 + n2) * sets > 200000) {
-          // too many workgroups to simulate: whole rounds
-          const int64_t w = (n1 + n2) * sets;
-          span = (w + cus - 1) / cus * cost(n1 ? r1 : r2, 1024);
+        Dispatch d(cus);
+        if (n2 == 0) {
+          d.run((n1 - 1) * sets, cost(r1, 1024));
+          d.run(sets, cost(r1, last));
         } else {
-          heap.assign(cus, 0);
-          auto run = [&](int64_t jobs, int64_t t) {
-            for (int64_t k = 0; k < jobs; ++k) {
-              std::pop_heap(heap.begin(), heap.end(), std::greater<int64_t>());
-              heap.back() += t;
-              std::push_heap(heap.begin(), heap.end(), std::greater<int64_t>());
-            }
-          };
-          if (n2 == 0) {
-            run((n1 - 1) * sets, cost(r1, 1024));
-            run(sets, cost(r1, last));
-          } else {
-            run(n1 * sets, cost(r1, 1024));
-            run((n2 - 1) * sets, cost(r2, 1024));
-            run(sets, cost(rem ? (int)rem : r2, last));  // the block with the last record
-          }
-          span = *std::max_element(heap.begin(), heap.end());
+          d.run(n1 * sets, cost(r1, 1024));
+          d.run((n2 - 1) * sets, cost(r2, 1024));
+          d.run(sets, cost(rem ? (int)rem : r2, last));  // the block with the last record
         }
+        const int64_t span = d.span();
         if (span < best_span) {
           best_span = span;
           best.r1 = r1;
