@@ -314,7 +314,9 @@ def run_level_mix(args, cfg, cd, x, shp, stream):
     of the layers), then one cg_decode of the records of a per-chunk level mix
     drawn from the seed. Step = that decode with the references in chunk
     order (levels interleaved); the same records referenced in runs of one
-    level are timed beside it."""
+    level are timed beside it. The two orders alternate, two turns each of
+    `steps` decodes; "steps" counts the timed decodes of the interleaved
+    order."""
     import numpy as np
     import torch
 
@@ -365,8 +367,13 @@ def run_level_mix(args, cfg, cd, x, shp, stream):
         call = float(np.mean([ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]))
         return wall, call, float(np.mean([t.elapsed_ms() for t in kt]))
 
-    wall_r, call_r, kern_r = timed("runs")
-    wall, call, kern = timed("mixed")
+    # the two orders alternate (twice each), so neither gets the warmer or
+    # cooler part of the run
+    res_o = {"runs": [], "mixed": []}
+    for name in ("runs", "mixed", "runs", "mixed"):
+        res_o[name].append(timed(name))
+    wall, call, kern = (float(np.mean(v)) for v in zip(*res_o["mixed"]))
+    wall_r, call_r, kern_r = (float(np.mean(v)) for v in zip(*res_o["runs"]))
     # correctness of this run: sampled (layer, K|V, head) slices against
     # numpy's dequant(quant(x)) with each chunk's own level
     rng = np.random.default_rng(2)
@@ -391,7 +398,7 @@ def run_level_mix(args, cfg, cd, x, shp, stream):
         "value": round(fp16_bytes / (wall / args.steps) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": 2 * args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 3),
         "higher_is_better": True,
