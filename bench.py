@@ -15,7 +15,10 @@ workload as bfloat16 elements (the fp16 draw rounded to bfloat16);
 --robust builds robust tables from the first quarter of the tokens only
 (calibration data) and encodes the whole cache with them; --attend times
 the restore-and-consume step instead: cg_decode_paged of every chunk into a
-paged pool, then cg_attend_paged of one new token per layer over it.
+paged pool, then cg_attend_paged of one new token per layer over it;
+--level-mix encodes every chunk at the three quality presets and times
+cg_decode of a seeded per-chunk level mix (with --config long: the
+80K-token multi-level workload).
 """
 from __future__ import annotations
 
