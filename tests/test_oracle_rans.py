@@ -58,6 +58,52 @@ def test_hand_derived_examples():
         assert rc == O.OK and np.array_equal(back, q), e["name"]
 
 
+def lane_example(e):
+    q = np.array([ln["q"] for ln in e["lanes"]], dtype=np.int32)
+    f = np.stack([table_from(ln["f"]) for ln in e["lanes"]])
+    return q, f, np.array(e["words"], dtype=np.uint16)
+
+
+def test_hand_derived_lane_examples():
+    """Different data on every lane: within one token the renorm words come
+    before the escape payloads, each block in ascending lane order, and a
+    token's words come before the next token's (hand-derived streams)."""
+    for e in json.load(open(GOLDEN))["lane_examples"]:
+        q, f, want = lane_example(e)
+        assert len(e["lanes"]) == 64 and q.shape == (64, 3)
+        words = O.encode_group_q(q, f)
+        assert np.array_equal(words, want), e["name"]
+        rc, back = O.decode_group_q(want, 3, f)
+        assert rc == O.OK and np.array_equal(back, q), e["name"]
+
+
+def test_lane_examples_tell_orders_apart():
+    """The goldens are not blind to the orders they pin: the stream with the
+    renorm and escape blocks swapped, or with either block in descending
+    lane order, is a different stream, and the oracle decoder rejects it or
+    decodes other values."""
+    e = json.load(open(GOLDEN))["lane_examples"][0]
+    q, f, want = lane_example(e)
+    cls = np.arange(64) % 4
+    n_r = int(np.isin(cls, (0, 2)).sum())
+    n_e = int(np.isin(cls, (1, 2)).sum())
+    head, ren, esc = want[:192], want[192:192 + n_r], want[192 + n_r:]
+    assert len(esc) == n_e
+    variants = [np.concatenate([head, esc, ren]), np.concatenate([head, ren[::-1], esc]),
+                np.concatenate([head, ren, esc[::-1]])]
+    for v in variants:
+        assert not np.array_equal(v, want)
+        rc, back = O.decode_group_q(v, 3, f)
+        assert rc != O.OK or not np.array_equal(back, q)
+    # token order: the second example's renorm words (token 1) precede its
+    # escape payloads (token 2)
+    e2 = json.load(open(GOLDEN))["lane_examples"][1]
+    q2, f2, want2 = lane_example(e2)
+    swapped = np.concatenate([want2[:192], want2[224:], want2[192:224]])
+    rc, back = O.decode_group_q(swapped, 3, f2)
+    assert rc != O.OK or not np.array_equal(back, q2)
+
+
 def random_q(rng, n, spread, jumps=0.0):
     q = np.zeros((64, n), dtype=np.int64)
     q[:, 0] = rng.integers(-32768, 32768, size=64)
