@@ -221,14 +221,16 @@ cg_status cg_decode_paged(const cg_shape* shape, int32_t n_levels, const cg_leve
  * slice) and decodes that set's groups of a block of records; records
  * [0, split) go in blocks of records_per_block, the rest in blocks of
  * records_per_block2, and a block's groups are dealt to 16 wavefronts that
- * decode up to three of them as interleaved chains. The plan minimises a
- * simulated dispatch over the current device's compute units (256 when no
- * device is visible). Writes out_host[3] = {records_per_block, split,
- * records_per_block2}. Returns CG_ERR_INVALID_ARG for n_refs < 1, a null
- * pointer or n_levels outside 1..8, and the shape and level checks of
+ * decode up to three of them at a time as interleaved chains (a layer group
+ * of more than 48 layers takes several rounds). The plan minimises a
+ * simulated dispatch over compute_units compute units; compute_units <= 0
+ * means those of the current device (256 when no device is visible), which
+ * is what the decoders plan with. Writes out_host[3] = {records_per_block,
+ * split, records_per_block2}. Returns CG_ERR_INVALID_ARG for n_refs < 1, a
+ * null pointer or n_levels outside 1..8, and the shape and level checks of
  * cg_decode. */
 cg_status cg_decode_plan(const cg_shape* shape, int32_t n_levels, const cg_level* levels, int32_t n_refs,
-                         int32_t* out_host);
+                         int32_t compute_units, int32_t* out_host);
 
 /* Streaming fill of a paged cache ("CacheGen实战" 2.3: a receive stage, a
  * parallel GPU decode stage and a fill stage run as a pipeline). Records

@@ -138,7 +138,7 @@ def lib():
         "cg_make_refs": (i32, [P, P, i32, i32, P, P]),
         "cg_decode": (i32, [sp, i32, lp, P, P, i32, P, P, pp, P]),
         "cg_decode_paged": (i32, [sp, i32, lp, P, P, i32, P, i64, P, P, pp, P]),
-        "cg_decode_plan": (i32, [sp, i32, lp, i32, P]),
+        "cg_decode_plan": (i32, [sp, i32, lp, i32, i32, P]),
         "cg_copy": (i32, [P, P, u64, P]),
         "cg_select_level": (i32, [ctypes.c_double]),
         "cg_recency_levels": (i32, [i64, i64, i64, P]),
@@ -262,12 +262,13 @@ def cg_decode_paged(shp, levels, tables, refs, n_refs, pool, num_blocks, block_t
     _check("cg_decode_paged", rc)
 
 
-def cg_decode_plan(shp, levels, n_refs):
-    """(records_per_block, split, records_per_block2) of the decode dispatch."""
+def cg_decode_plan(shp, levels, n_refs, compute_units=0):
+    """(records_per_block, split, records_per_block2) of the decode dispatch
+    over compute_units compute units (0: the current device's)."""
     arr = (cg_level * len(levels))(*[lv.c for lv in levels])
     out = np.zeros(3, dtype=np.int32)
     _check("cg_decode_plan", lib().cg_decode_plan(ctypes.byref(shp), len(levels), arr, int(n_refs),
-                                                  out.ctypes.data))
+                                                  int(compute_units), out.ctypes.data))
     return int(out[0]), int(out[1]), int(out[2])
 
 

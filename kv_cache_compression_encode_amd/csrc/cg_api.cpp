@@ -148,8 +148,7 @@ struct Dispatch {
 };
 
 template <class Cost>
-static BlockPlan plan_blocks(int64_t n_rec, int64_t sets, int max_r, int64_t last, Cost cost) {
-  const int cus = compute_units();
+static BlockPlan plan_blocks(int cus, int64_t n_rec, int64_t sets, int max_r, int64_t last, Cost cost) {
   BlockPlan best;
   int64_t best_span = INT64_MAX;
   for (int r1 = 1; r1 <= max_r && r1 <= n_rec; ++r1) {
@@ -198,25 +197,28 @@ static int64_t last_len(const Shape& s, bool ends_at_last_chunk) {
 }
 
 // Decode: a workgroup holds R records x (layers of its group) groups, dealt
-// to its 16 wavefronts, so a wavefront runs c = ceil(items / 16) <= 3
-// interleaved chains; workgroup times per chain count are measured on gfx950
-// (3 chains = 1000). A block ending with a short record runs all chains for
-// that length, then one chain fewer.
-static void plan_decode(const Shape& s, const cg_level& lv, int32_t n_refs, DecodeArgs* a) {
+// to its 16 wavefronts, so a wavefront runs c = ceil(items / 16) chains,
+// at most three interleaved at a time (more in further rounds of three);
+// workgroup times per chain count are measured on gfx950 (3 chains = 1000).
+// A block ending with a short record runs all chains for that length, then
+// one chain fewer.
+static void plan_decode(const Shape& s, const cg_level& lv, int32_t n_refs, int cus, DecodeArgs* a) {
   static const int kWgCost[kChains + 1] = {0, 380, 710, 1000};
   const int lg_max = max_layers_per_group(s, lv);
   auto chains = [&](int r) { return (r * lg_max + kWaves - 1) / kWaves; };
+  auto wg_cost = [&](int c) { return (int64_t)(c / kChains) * kWgCost[kChains] + kWgCost[c % kChains]; };
   int max_r = 1;
   while (max_r < kMaxRefsPerBlock && chains(max_r + 1) <= kChains) ++max_r;
   auto cost = [&](int r, int64_t last) {
-    const int64_t rest = r > 1 ? kWgCost[chains(r - 1)] : 0;
-    return (int64_t)kWgCost[chains(r)] * last / 1024 + rest * (1024 - last) / 1024 + 5;
+    const int64_t rest = r > 1 ? wg_cost(chains(r - 1)) : 0;
+    return wg_cost(chains(r)) * last / 1024 + rest * (1024 - last) / 1024 + 5;
   };
-  const BlockPlan p = plan_blocks(n_refs, (int64_t)lv.n_groups * 2 * s.H * s.S, max_r,
+  const BlockPlan p = plan_blocks(cus, n_refs, (int64_t)lv.n_groups * 2 * s.H * s.S, max_r,
                                   last_len(s, n_refs == n_chunks(s.T, s.C)), cost);
   a->refs_per_block = p.r1;
   a->split = p.split;
   a->refs_per_block2 = p.r2;
+  a->item_rounds = (int32_t)((p.r1 * lg_max + kWaves * kChains - 1) / (kWaves * kChains));
 }
 
 // Encode: a workgroup holds R chunks x (layers of its group) groups, dealt
@@ -233,7 +235,7 @@ static void plan_encode(const Shape& s, const cg_level& lv, int64_t chunk_end, i
     }
     return worst + 5;
   };
-  const BlockPlan p = plan_blocks(n, (int64_t)lv.n_groups * 2 * s.H * s.S, 4,
+  const BlockPlan p = plan_blocks(compute_units(), n, (int64_t)lv.n_groups * 2 * s.H * s.S, 4,
                                   last_len(s, chunk_end == n_chunks(s.T, s.C)), cost);
   a->chunks_per_block = p.r1;
   a->split = p.split;
@@ -474,7 +476,9 @@ static cg_status decode_common(const cg_shape* shape, int32_t n_levels, const cg
     a->n_groups[k] = levels[k].n_groups;
     if (levels[k].n_groups > g_max) g_max = levels[k].n_groups;
   }
-  if ((uint64_t)n_refs * g_max * 2 * s.H * s.S * n_levels >= (1ull << 31)) return CG_ERR_UNSUPPORTED;
+  if ((uint64_t)n_refs * g_max * 2 * s.H * s.S * n_levels * ((s.L + kWaves * kChains - 1) / (kWaves * kChains)) >=
+      (1ull << 31))
+    return CG_ERR_UNSUPPORTED;
   a->s = s;
   a->refs = refs_dev;
   a->n_refs = n_refs;
@@ -486,7 +490,7 @@ static cg_status decode_common(const cg_shape* shape, int32_t n_levels, const cg
   int widest = 0;
   for (int k = 1; k < n_levels; ++k)
     if (max_layers_per_group(s, levels[k]) > max_layers_per_group(s, levels[widest])) widest = k;
-  plan_decode(s, levels[widest], n_refs, a);
+  plan_decode(s, levels[widest], n_refs, compute_units(), a);
   a->per_level = n_levels > 1;
   a->n_tables = n_levels;
   a->g_max = g_max;
@@ -495,7 +499,7 @@ static cg_status decode_common(const cg_shape* shape, int32_t n_levels, const cg
 }
 
 cg_status cg_decode_plan(const cg_shape* shape, int32_t n_levels, const cg_level* levels, int32_t n_refs,
-                         int32_t* out_host) {
+                         int32_t compute_units_hint, int32_t* out_host) {
   Shape s;
   cg_status rc = check_shape(shape, &s);
   if (rc != CG_OK) return rc;
@@ -506,7 +510,7 @@ cg_status cg_decode_plan(const cg_shape* shape, int32_t n_levels, const cg_level
   for (int k = 1; k < n_levels; ++k)
     if (max_layers_per_group(s, levels[k]) > max_layers_per_group(s, levels[widest])) widest = k;
   DecodeArgs a;
-  plan_decode(s, levels[widest], n_refs, &a);
+  plan_decode(s, levels[widest], n_refs, compute_units_hint > 0 ? compute_units_hint : compute_units(), &a);
   out_host[0] = a.refs_per_block;
   out_host[1] = a.split;
   out_host[2] = a.refs_per_block2;

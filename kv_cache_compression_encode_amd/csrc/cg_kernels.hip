@@ -1718,6 +1718,8 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const Shape s = a.s;
   int64_t bid = blockIdx.x;
+  const int round = (int)(bid % a.item_rounds);  // which 48 of the block's groups
+  bid /= a.item_rounds;
   const int j = (int)(bid % s.S);
   bid /= s.S;
   const int h = (int)(bid % s.H);
@@ -1830,23 +1832,29 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
     ++nrec;
   }
   if (nrec == 0) return;
+  // items = (record, k-th layer of the group), record-major; this workgroup
+  // decodes items [48 round, 48 round + 48) (a layer group of more than 48
+  // layers spreads one record over several workgroups)
+  const int lg_count = layers_in_group(blob, G, s.L, g, lane);
+  constexpr int kRound = kWaves * kChains;
+  const int base = round * kRound;
+  const int items = nrec * lg_count - base < kRound ? nrec * lg_count - base : kRound;
+  if (items <= 0) return;
 
   // the set's decoder tables, one contiguous 128 KB block
   const size_t set = (((size_t)g * 2 + kv) * s.H + h) * s.S + j;
   const uint4* dsrc = reinterpret_cast<const uint4*>(
       reinterpret_cast<const uint32_t*>(blob + tb_dec_offset(s.L, s.H, s.D, G)) + set * (kDecDwords * 64));
   for (int u = tid; u < kDecDwords * 64 / 4; u += kDecThreads) reinterpret_cast<uint4*>(tabs)[u] = dsrc[u];
-  const int lg_count = layers_in_group(blob, G, s.L, g, lane);
   const float step = blob_step(blob, g);
   if (tid < kWaves) left[tid] = 0x7FFFFFFF;
   __syncthreads();
 
-  // items = (record, k-th layer of the group), record-major; wavefront w
-  // takes items w, w + 16, w + 32. Deeper layers code more bits per value, so
-  // the layer order is turned around in the second record and rotated by half
-  // in the third: each wavefront gets a shallow, a deep and a middle layer
-  // rather than the same depth three times.
-  const int items = nrec * lg_count;
+  // wavefront w takes items w, w + 16, w + 32 of the workgroup's. Deeper
+  // layers code more bits per value, so the layer order is turned around in
+  // the second record and rotated by half in the third: each wavefront gets
+  // a shallow, a deep and a middle layer rather than the same depth three
+  // times.
   const int mine = wave < items ? (items - 1 - wave) / kWaves + 1 : 0;
   if (mine == 0) {
     if (lane == 0) left[wave] = 0;
@@ -1856,7 +1864,7 @@ __global__ void __launch_bounds__(kDecThreads) k_decode(DecodeArgs a) {
 #pragma unroll
   for (int k = 0; k < kChains; ++k) {
     if (k < mine) {
-      const int it = wave + k * kWaves;
+      const int it = base + wave + k * kWaves;
       const int ri = it / lg_count;
       GroupRef gr = ri == 0 ? rr0 : ri == 1 ? rr1 : rr2;
       int li = it - ri * lg_count;
@@ -2246,7 +2254,8 @@ hipError_t launch_attend_reduce(const AttendArgs& a, hipStream_t st) {
 hipError_t launch_decode(const DecodeArgs& a, bool paged, hipStream_t st) {
   const uint64_t rblocks = (uint64_t)(a.split / a.refs_per_block) +
                            (uint64_t)(a.n_refs - a.split + a.refs_per_block2 - 1) / a.refs_per_block2;
-  const uint64_t blocks = rblocks * (a.per_level ? a.n_tables : 1) * a.g_max * 2 * a.s.H * a.s.S;
+  const uint64_t blocks =
+      rblocks * (a.per_level ? a.n_tables : 1) * a.g_max * 2 * a.s.H * a.s.S * a.item_rounds;
   const bool bf = a.s.dt == kDtypeBf16;
   if (paged && bf)
     hipLaunchKernelGGL((k_decode<true, true>), dim3((unsigned)blocks), dim3(kDecThreads), 0, st, a);

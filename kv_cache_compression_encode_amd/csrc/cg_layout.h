@@ -219,6 +219,9 @@ struct DecodeArgs {
   // block decodes only the records of its copy's set (records of several
   // levels in any order); otherwise a block's set is its first record's
   int32_t per_level;
+  // workgroups per block of records and table set: a block's groups are
+  // decoded 48 (16 wavefronts x 3 chains) per workgroup
+  int32_t item_rounds;
   int32_t n_tables;
   int32_t g_max;
   const uint8_t* tables[kMaxLevels];

@@ -12,9 +12,14 @@ LIB = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libcg.so not built")
 
 # measured workgroup times per chains per wavefront (3 chains = 1000), as the
-# library plans with them; 16 wavefronts, at most 3 records and 3 chains
+# library plans with them; 16 wavefronts, at most 3 records, chains run three
+# at a time (more than three: further rounds)
 WG_COST = [0, 380, 710, 1000]
 CUS = 256
+
+
+def wg_cost(c):
+    return (c // 3) * WG_COST[3] + WG_COST[c % 3]
 
 
 def heap_plan(n_rec, sets, lg_max, last):
@@ -24,8 +29,8 @@ def heap_plan(n_rec, sets, lg_max, last):
         max_r += 1
 
     def cost(r, lst):
-        rest = WG_COST[chains(r - 1)] if r > 1 else 0
-        return WG_COST[chains(r)] * lst // 1024 + rest * (1024 - lst) // 1024 + 5
+        rest = wg_cost(chains(r - 1)) if r > 1 else 0
+        return wg_cost(chains(r)) * lst // 1024 + rest * (1024 - lst) // 1024 + 5
 
     best = None
     for r1 in range(1, min(max_r, n_rec) + 1):
@@ -58,6 +63,7 @@ CASES = [
     (16, 1, 64, 1024, 256), (16, 64, 64, 35, 3), (16, 64, 64, 26, 2), (16, 32, 64, 181, 16),
     (16, 8, 128, 32768, 1536), (11, 32, 128, 8192, 1536), (16, 48, 128, 5000, 300),
     (8, 64, 64, 700, 50), (33, 16, 64, 900, 64), (5, 128, 128, 3000, 200), (16, 96, 64, 97, 7),
+    (64, 8, 128, 4096, 512), (100, 2, 64, 333, 33),
 ]
 
 
@@ -67,4 +73,4 @@ def test_plan_matches_per_workgroup_simulation(L, H, D, T, Cc):
     lv = C.Level(2, [0] * L, [0.7])
     n = -(-T // Cc)
     last = (T - (n - 1) * Cc) * 1024 // Cc
-    assert C.cg_decode_plan(C.shape(L, H, D, T, Cc), [lv], n) == heap_plan(n, 2 * H * (D // 64), L, last)
+    assert C.cg_decode_plan(C.shape(L, H, D, T, Cc), [lv], n, CUS) == heap_plan(n, 2 * H * (D // 64), L, last)

@@ -28,6 +28,11 @@ CASES = [
     ("bf16-wide-range", 2, 1, 64, 300, 100, [0, 1], [2e5, 7e5], BF16, 0,
      lambda: synth.random_kv_bf16(2, 1, 64, 300, 32, scale=1e6), None),
     ("bf16-every-pattern", 1, 1, 64, 1024, 256, [0], [0.37], BF16, 0, all_bf16_patterns, None),
+    # every bf16 input at each of the nine preset steps ("CacheGen实战" 3.1),
+    # whose quotients take the multiply or one-FMA paths
+    ("bf16-every-pattern-presets", 9, 1, 64, 1024, 256, list(range(9)),
+     [0.3, 0.8, 1.2, 0.5, 1.0, 1.5, 0.8, 1.5, 2.0], BF16, 0,
+     lambda: np.concatenate([all_bf16_patterns()] * 9), None),
     ("robust-fp16", 3, 2, 64, 500, 128, [0, 1, 2], [0.5, 1.0, 1.5], 0, ROBUST,
      lambda: synth.random_kv(3, 2, 64, 500, 33, scale=8.0, rho=0.5),
      lambda: synth.random_kv(3, 2, 64, 260, 34, scale=1.0, rho=0.99)),

@@ -1,7 +1,10 @@
 """Edge cases of the codec on the GPU against the oracle, byte by byte:
-every fp16 bit pattern (NaN, +-Inf, subnormals, saturation), a tensor where
-every delta needs an escape (the worst-case stream size), one layer group per
-layer, and the largest group count (255)."""
+every fp16 bit pattern (NaN, +-Inf, subnormals, saturation) at a step that
+takes the IEEE divide and at each of the nine preset steps ("CacheGen实战"
+section 3.1: 0.3/0.8/1.2, 0.5/1.0/1.5, 0.8/1.5/2.0), whose quotients take
+the multiply or one-FMA paths, a tensor where every delta needs an escape
+(the worst-case stream size), one layer group per layer, and the largest
+group count (255)."""
 import numpy as np
 import pytest
 
@@ -13,6 +16,13 @@ pytestmark = pytest.mark.gpu
 def every_fp16_pattern():
     k = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(1024, 64)
     return np.stack([k, k[::-1, ::-1]])[None, :, None].copy().view(np.float16)
+
+
+PRESET_STEPS = [0.3, 0.8, 1.2, 0.5, 1.0, 1.5, 0.8, 1.5, 2.0]
+
+
+def every_fp16_pattern_per_layer(L):
+    return np.concatenate([every_fp16_pattern()] * L)
 
 
 def all_escapes():
@@ -28,6 +38,8 @@ def many_groups(L, T, seed):
 CASES = [
     # name, L, H, D, T, C, layer_group, steps, X
     ("every-fp16-pattern", 1, 1, 64, 1024, 256, [0], [0.37], every_fp16_pattern),
+    ("every-fp16-pattern-presets", 9, 1, 64, 1024, 256, list(range(9)), PRESET_STEPS,
+     lambda: every_fp16_pattern_per_layer(9)),
     ("all-escapes", 2, 1, 64, 300, 100, [0, 0], [4.0], all_escapes),
     ("group-per-layer", 64, 1, 64, 40, 16, list(range(64)), [0.3 + 0.025 * g for g in range(64)],
      lambda: many_groups(64, 40, 62)),
@@ -53,6 +65,15 @@ def test_tables_and_stats(pair):
     assert np.array_equal(g["stats"].cpu().numpy().astype(np.uint64), o["stats"])
     if name == "every-fp16-pattern":
         assert int(o["stats"][2]) == 2 * 2046  # every NaN pattern, in K and in V
+    if name == "every-fp16-pattern-presets":
+        assert int(o["stats"][2]) == 9 * 2 * 2046
+        # the quotient paths the tables chose (library lookup section, right
+        # after the format section: u32 per layer group, bit 1 = multiply,
+        # bit 0 = one-FMA correction, proven exact over every input): both
+        # fast paths are exercised, so the byte checks cover them
+        qoff = -(-fb // 256) * 256
+        qf = U.u8(g["tables"])[qoff:qoff + 4 * 9].view(np.uint32)
+        assert (qf & 2).any() and (qf == 1).any(), qf
     if name == "all-escapes":
         assert int(o["stats"][3]) > 0.95 * 2 * 2 * 299 * 64
 

@@ -17,6 +17,10 @@ CASES = [
     ("chunk-7", 2, 1, 64, 37, 7, [0, 0], [1.0], 3),
     ("d192-single-chunk", 1, 3, 192, 100, 100, [0], [0.3], 4),
     ("many-layers", 17, 1, 64, 129, 128, [l // 6 for l in range(17)], [0.3, 0.8, 1.2], 5),
+    # layer groups wider than one workgroup round (16 wavefronts x 3 chains):
+    # 64 layers in one group (two rounds), 60 + 40 layers (rounds of 48 + 12)
+    ("64-layers-one-group", 64, 1, 64, 40, 16, [0] * 64, [0.8], 6),
+    ("100-layers-two-groups", 100, 1, 64, 33, 33, [0] * 60 + [1] * 40, [0.5, 1.5], 7),
 ]
 
 
@@ -67,3 +71,24 @@ def test_decode_bit_exact(pair):
     assert g["st_dec"] == 0
     y = g["y"].cpu().numpy().view(np.uint16)
     assert np.array_equal(y, o["Y"])
+
+
+def test_paged_decode_bit_exact(pair):
+    """The paged decoder over a seeded random block table gives the oracle's
+    pool; untouched blocks keep their fill."""
+    args, g, o = pair
+    L, H, D, T, Cc, lg, steps = args[:7]
+    nb = -(-T // 16)
+    NB = nb + 3
+    bt = np.random.default_rng(11).permutation(NB)[:nb].astype(np.int32)
+    pool = U.torch.full((L, 2, NB, H, 16, D), 0x7E00, dtype=U.torch.int16, device="cuda").view(
+        g["x"].dtype)
+    bt_dev = U.torch.from_numpy(bt).cuda()
+    refs, n = g["cd"].refs_for(g["out"], g["offs"])
+    g["cd"].decode_paged([g["lv"]], [g["tables"]], refs, n, pool, bt_dev)
+    assert g["cd"].read_status() == 0
+    want = np.full((L, 2, NB, H, 16, D), 0x7E00, dtype=np.uint16)
+    for c in range(len(o["offs"]) - 1):
+        rec = o["data"][int(o["offs"][c]):int(o["offs"][c + 1])]
+        assert U.O.decode_chunk_paged(o["shp"], o["blob"], rec, want, bt) == U.O.OK
+    assert np.array_equal(pool.cpu().view(U.torch.int16).numpy().view(np.uint16), want)
