@@ -694,10 +694,18 @@ cg_status cg_stream_decode_paged(const cg_shape* shape, int32_t n_levels, const 
   return hip_status(e);
 }
 
+// Bandwidth a level needs, in Gbit/s ("CacheGen实战" 2.2: the sender
+// switches to a cheaper level as the measured link slows; reading of the
+// page's garbled thresholds): level k is taken when the measured bandwidth
+// exceeds kLevelNeedGbps[k], trying the highest quality first; the last
+// level (fast) needs nothing. A NaN bandwidth exceeds nothing.
+static const double kLevelNeedGbps[] = {5.0, 1.0};
+static const int32_t kLevels = (int32_t)(sizeof(kLevelNeedGbps) / sizeof(kLevelNeedGbps[0])) + 1;
+
 int32_t cg_select_level(double bandwidth_gbps) {
-  if (bandwidth_gbps > 5.0) return 0;
-  if (bandwidth_gbps > 1.0) return 1;
-  return 2;  // also NaN
+  int32_t k = 0;
+  while (k < kLevels - 1 && !(bandwidth_gbps > kLevelNeedGbps[k])) ++k;
+  return k;
 }
 
 cg_status cg_recency_levels(int64_t n_chunks, int64_t near_chunks, int64_t far_chunks,
