@@ -1,5 +1,6 @@
 """Full-size workloads through the C ABI, in the launch configuration the
-benchmark times, checked on sampled outputs the oracle computes one by one."""
+benchmark times, checked against the oracle over the whole tensor: every
+table, every record byte and every decoded element (tests/fullsize.py)."""
 import numpy as np
 import pytest
 
@@ -23,6 +24,10 @@ def run_level(cd, x, lvd):
     return lv, tables, out, offs
 
 
+def host_bits(t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
 @pytest.mark.parametrize("name", ["7b", "34b"])
 def test_contiguous_roundtrip(name):
     U.need_gpu()
@@ -36,19 +41,26 @@ def test_contiguous_roundtrip(name):
     refs, n = cd.refs_for(out, offs)
     y = cd.decode([lv], [tables], refs, n)
     assert cd.read_status() == 0
-    rng = np.random.default_rng(1)
+    del x
     blob = U.u8(tables[:cd.format_bytes(lv)])
     o = offs.cpu().numpy()
-    F.check_tables(cfg, lvd, X, blob, rng)
-    F.check_groups(cfg, X, blob, lambda a, b: U.u8(out[a:b]), o, rng)
+    out_h = U.u8(out)
+    nt = F.check_all_tables(cfg, lvd, X, blob)
+    nb = F.check_all_records(cfg, X, blob, lambda k: out_h[int(o[k]):int(o[k + 1])], list(range(cfg.n_chunks)))
+    y_h = host_bits(y)
+    del y
     steps = [lvd.steps[g] for g in lvd.layer_group]
-    F.check_slices(cfg, steps, X, lambda l, kv, h: y[l, kv, h].cpu().numpy().view(np.uint16), rng)
+    ne = F.check_all_decoded(cfg, X, steps, lambda l: y_h[l])
     ratio = X.nbytes / int(o[-1])
-    print("%s ratio %.3f:1" % (name, ratio), flush=True)
+    print("%s: %d tables, %d record bytes, %d decoded elements identical; ratio %.3f:1" % (
+        name, nt, nb, ne, ratio), flush=True)
     assert 2.0 < ratio < 20.0
 
 
 def test_long_context_three_levels_mixed():
+    """Three levels of the 80K-token cache: every table of every level, two
+    whole records per level (the short last chunk and one other), and every
+    element of a decode that mixes the levels per chunk."""
     U.need_gpu()
     cfg = synth.CONFIGS["long"]
     X = synth.generate(cfg)
@@ -60,25 +72,31 @@ def test_long_context_three_levels_mixed():
     for k, lvd in enumerate(cfg.levels):
         lv, tables, out, offs = run_level(cd, x, lvd)
         blob = U.u8(tables[:cd.format_bytes(lv)])
-        F.check_tables(cfg, lvd, X, blob, rng, n=3)
-        F.check_groups(cfg, X, blob, lambda a, b, out=out: U.u8(out[a:b]), offs.cpu().numpy(), rng, n=2)
-        print("level", lvd.name, "ratio %.3f" % (X.nbytes / int(offs[-1])), flush=True)
+        F.check_all_tables(cfg, lvd, X, blob)
+        o = offs.cpu().numpy()
+        picks = [cfg.n_chunks - 1, int(rng.integers(cfg.n_chunks - 1))]
+        F.check_all_records(cfg, X, blob, lambda i, out=out, o=o, p=picks: U.u8(out[int(o[p[i]]):int(o[p[i] + 1])]),
+                            picks)
+        print("level %s: tables and chunks %s identical, ratio %.3f" % (lvd.name, picks, X.nbytes / int(o[-1])),
+              flush=True)
         lvs.append(lv)
         tabs.append(tables)
         outs.append((out, offs))
+    del x
     mix = synth.level_mix(cfg)
     parts = [(outs[int(m)][0], outs[int(m)][1], [c], int(m)) for c, m in enumerate(mix)]
     refs, n = cd.make_refs(parts)
     y = cd.decode(lvs, tabs, refs, n)
     assert cd.read_status() == 0
-    # per chunk the reconstruction uses that chunk's level
-    for _ in range(3):
-        c = int(rng.integers(cfg.n_chunks))
-        lvd = cfg.levels[int(mix[c])]
-        steps = [lvd.steps[g] for g in lvd.layer_group]
+    y_h = host_bits(y)
+    del y
+    token_steps = []
+    for c, m in enumerate(mix):
+        lvd = cfg.levels[int(m)]
         t = slice(c * cfg.chunk_tokens, min((c + 1) * cfg.chunk_tokens, cfg.tokens))
-        F.check_slices(cfg, steps, X, lambda l, kv, h: y[l, kv, h].cpu().numpy().view(np.uint16), rng,
-                       n=2, tokens=t)
+        token_steps.append((t, [lvd.steps[g] for g in lvd.layer_group]))
+    ne = F.check_all_decoded(cfg, X, None, lambda l: y_h[l], token_steps=token_steps)
+    print("long: %d decoded elements of the level mix identical" % ne, flush=True)
 
 
 def test_stream_paged():
@@ -105,17 +123,11 @@ def test_stream_paged():
     refs, n = cd.refs_for(out, offs)
     cd.decode_paged([lv], [tables], refs, n, pool, torch.from_numpy(bt).cuda())
     assert cd.read_status() == 0
-    rng = np.random.default_rng(3)
-    steps = [lvd.steps[g] for g in lvd.layer_group]
-
-    def y_slice(l, kv, h):
-        blocks = pool[l, kv, torch.from_numpy(bt.astype(np.int64)).cuda(), h]  # [T/16][16][D]
-        return blocks.reshape(cfg.tokens, cfg.head_dim).cpu().numpy().view(np.uint16)
-
-    F.check_slices(cfg, steps, X, y_slice, rng)
     blob = U.u8(tables[:cd.format_bytes(lv)])
     o = offs.cpu().numpy()
-    F.check_groups(cfg, X, blob, lambda a, b: U.u8(out[a:b]), o, rng, n=3)
+    out_h = U.u8(out[:int(o[-1])])
+    F.check_all_tables(cfg, lvd, X, blob)
+    F.check_all_records(cfg, X, blob, lambda k: out_h[int(o[k]):int(o[k + 1])], list(range(cfg.n_chunks)))
 
     # the same records streamed from pinned host memory into a second pool
     host = torch.empty(int(o[-1]), dtype=torch.uint8).pin_memory()
@@ -139,19 +151,33 @@ def test_stream_paged():
         print("%s: streamed %d records, %.1f MB in %.2f ms (%.1f GB/s host-to-device incl. decode)" % (
             turn, n, o[-1] / 1e6, ms, o[-1] / ms / 1e6), flush=True)
         assert torch.equal(pool2.view(torch.int16), pool.view(torch.int16))
+    del pool2
+
+    # every element of the pool, gathered through the block table
+    steps = [lvd.steps[g] for g in lvd.layer_group]
+    pool_h = host_bits(pool)
+    del pool
+    T, H, D = cfg.tokens, cfg.kv_heads, cfg.head_dim
+
+    def y_layer(l):
+        blocks = pool_h[l][:, bt]  # [2][T/16][H][16][D]
+        return blocks.transpose(0, 2, 1, 3, 4).reshape(2, H, T, D)
+
+    ne = F.check_all_decoded(cfg, X, steps, y_layer)
+    print("stream: %d pooled elements identical" % ne, flush=True)
 
 
 def test_34b_bf16_robust_calibration_tables():
     """The 34B workload as bfloat16 with robust tables built from its first
     quarter of tokens only (calibration data), every chunk encoded with them:
-    sampled tables, groups and decoded slices against the oracle."""
+    every table, record byte and decoded element against the oracle."""
     U.need_gpu()
     cfg = synth.CONFIGS["34b"]
     lvd = cfg.levels[0]
     X16 = synth.generate(cfg)
     x = U.to_dev(X16).to(torch.bfloat16)
     del X16
-    Xb = x.cpu().view(torch.int16).numpy().view(np.uint16)
+    Xb = host_bits(x)
     print("generated 34b bf16", flush=True)
     Tc = cfg.tokens // 4
     shp = C.shape(cfg.layers, cfg.kv_heads, cfg.head_dim, cfg.tokens, cfg.chunk_tokens, C.CG_DTYPE_BF16)
@@ -164,35 +190,16 @@ def test_34b_bf16_robust_calibration_tables():
     refs, n = cd.refs_for(out, offs)
     y = cd.decode([lv], [tables], refs, n)
     assert cd.read_status() == 0
-    rng = np.random.default_rng(3)
+    del x
     blob = U.u8(tables[:cd.format_bytes(lv)])
-    G = len(lvd.steps)
-    # tables: robust normalisation of the calibration counts
-    Xc = np.ascontiguousarray(Xb[:, :, :, :Tc, :])
-    ocshp = U.O.shape(cfg.layers, cfg.kv_heads, cfg.head_dim, Tc, cfg.chunk_tokens, U.O.BF16)
-    f = U.O.table_f(blob, ocshp, G)
-    for _ in range(4):
-        g, kv, h, d = int(rng.integers(G)), int(rng.integers(2)), int(rng.integers(cfg.kv_heads)), \
-            int(rng.integers(cfg.head_dim))
-        counts, _ = U.O.table_counts(ocshp, lvd.layer_group, lvd.steps, Xc, g, kv, h, d)
-        assert np.array_equal(f[g, kv, h, d], U.O.normalize(counts, robust=True)), (g, kv, h, d)
-    del Xc
-    # groups of the whole tensor coded with the calibration tables
-    oshp = U.O.shape(cfg.layers, cfg.kv_heads, cfg.head_dim, cfg.tokens, cfg.chunk_tokens, U.O.BF16)
     o = offs.cpu().numpy()
-    S = cfg.head_dim // 64
-    gpc = cfg.layers * 2 * cfg.kv_heads * S
-    for c in [cfg.n_chunks - 1] + [int(rng.integers(cfg.n_chunks)) for _ in range(3)]:
-        l, kv, h, j = (int(rng.integers(cfg.layers)), int(rng.integers(2)), int(rng.integers(cfg.kv_heads)),
-                       int(rng.integers(S)))
-        w = U.O.encode_group(oshp, blob, Xb, c, l, kv, h, j)
-        rec = U.u8(out[int(o[c]):int(o[c + 1])])
-        got = F.record_group(rec, gpc, ((l * 2 + kv) * cfg.kv_heads + h) * S + j)
-        assert np.array_equal(got, w), (c, l, kv, h, j)
-    # decoded slices
-    for _ in range(3):
-        l, kv, h = int(rng.integers(cfg.layers)), int(rng.integers(2)), int(rng.integers(cfg.kv_heads))
-        st = lvd.steps[lvd.layer_group[l]]
-        ref = F.npref.dequantize_bits(F.npref.quantize_bits(Xb[l, kv, h], st, 1), st, 1)
-        assert np.array_equal(y[l, kv, h].cpu().view(torch.int16).numpy().view(np.uint16), ref), (l, kv, h)
-    print("34b bf16 robust ratio %.3f:1" % (2 * Xb.size / int(o[-1])), flush=True)
+    out_h = U.u8(out[:int(o[-1])])
+    F.check_all_tables(cfg, lvd, Xb, blob, dtype=U.O.BF16, robust=True, tokens=Tc)
+    F.check_all_records(cfg, Xb, blob, lambda k: out_h[int(o[k]):int(o[k + 1])], list(range(cfg.n_chunks)),
+                        dtype=U.O.BF16)
+    y_h = host_bits(y)
+    del y
+    steps = [lvd.steps[g] for g in lvd.layer_group]
+    ne = F.check_all_decoded(cfg, Xb, steps, lambda l: y_h[l], dtype=1)
+    print("34b bf16 robust: %d decoded elements identical, ratio %.3f:1" % (ne, 2 * Xb.size / int(o[-1])),
+          flush=True)
