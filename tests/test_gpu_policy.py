@@ -1,8 +1,8 @@
 """Per-chunk level policies end to end on the GPU (the long-context workload
 cut to 8 chunks): bandwidth-adaptive record selection streamed into a paged
-cache, and recency-based encoding decoded as a level mix. Decoded values are
-compared with numpy's dequant(quant(x)) at each chunk's level, and sampled
-groups of the picked records with the oracle's encoder."""
+cache, and recency-based encoding decoded as a level mix. Every decoded
+value is compared with numpy's dequant(quant(x)) at its chunk's level, and
+every byte of the picked records with the oracle's encoding at that level."""
 import dataclasses
 
 import numpy as np
@@ -25,13 +25,14 @@ def workload():
     return cfg, synth.generate(cfg)
 
 
-def check_by_chunk(cfg, X, levels, y_slice, rng, n=3):
-    for _ in range(n):
-        c = int(rng.integers(cfg.n_chunks))
+def check_by_chunk(cfg, X, levels, y_layer):
+    """Every element of the decoded cache at its chunk's level."""
+    token_steps = []
+    for c in range(cfg.n_chunks):
         lvd = cfg.levels[int(levels[c])]
-        steps = [lvd.steps[g] for g in lvd.layer_group]
         t = slice(c * cfg.chunk_tokens, min((c + 1) * cfg.chunk_tokens, cfg.tokens))
-        F.check_slices(cfg, steps, X, y_slice, rng, n=2, tokens=t)
+        token_steps.append((t, [lvd.steps[g] for g in lvd.layer_group]))
+    F.check_all_decoded(cfg, X, None, y_layer, token_steps=token_steps)
 
 
 def test_bandwidth_adaptive_stream():
@@ -63,19 +64,20 @@ def test_bandwidth_adaptive_stream():
     torch.cuda.synchronize()
     del keep
     assert cd.read_status() == 0
-    rng = np.random.default_rng(5)
-    bt64 = torch.from_numpy(bt.astype(np.int64)).cuda()
+    pool_h = pool.cpu().view(torch.int16).numpy().view(np.uint16)
+    del pool
+    T, H, D = cfg.tokens, cfg.kv_heads, cfg.head_dim
 
-    def y_slice(l, kv, h):
-        blocks = pool[l, kv, bt64, h]
-        return blocks.reshape(-1, cfg.head_dim)[:cfg.tokens].cpu().numpy().view(np.uint16)
+    def y_layer(l):
+        blocks = pool_h[l][:, bt]  # [2][blocks][H][16][D]
+        return blocks.transpose(0, 2, 1, 3, 4).reshape(2, H, -1, D)[:, :, :T]
 
-    check_by_chunk(cfg, X, levels, y_slice, rng)
+    check_by_chunk(cfg, X, levels, y_layer)
     # the picked records are the oracle's, at each chunk's level
-    for c in (0, cfg.n_chunks - 1):
-        k = int(levels[c])
+    for k in range(len(cfg.levels)):
+        cs = [c for c in range(cfg.n_chunks) if int(levels[c]) == k]
         blob = U.u8(tabs[k][:cd.format_bytes(lvs[k])])
-        F.check_groups(cfg, X, blob, lambda a, b: recs[a:b], offs[c:c + 2], rng, n=2, chunks=[c])
+        F.check_all_records(cfg, X, blob, lambda i, cs=cs: recs[int(offs[cs[i]]):int(offs[cs[i] + 1])], cs)
     assert P.transfer_seconds(offs, trace) > 0
 
 
@@ -94,10 +96,11 @@ def test_recency_levels_mix():
     assert n == cfg.n_chunks
     y = cd.decode(lvs, tabs, refs, n)
     assert cd.read_status() == 0
-    rng = np.random.default_rng(6)
-    check_by_chunk(cfg, X, levels, lambda l, kv, h: y[l, kv, h].cpu().numpy().view(np.uint16), rng)
+    y_h = y.cpu().view(torch.int16).numpy().view(np.uint16)
+    check_by_chunk(cfg, X, levels, lambda l: y_h[l])
     # every segment's records are the oracle's at that level
     for b, e, k, out, offs in segs:
         blob = U.u8(tabs[k][:cd.format_bytes(lvs[k])])
-        F.check_groups(cfg, X, blob, lambda a, bb, out=out: U.u8(out[a:bb]), offs.cpu().numpy(), rng, n=1,
-                       chunks=list(range(b, e)))
+        o = offs.cpu().numpy()
+        F.check_all_records(cfg, X, blob, lambda i, out=out, o=o: U.u8(out[int(o[i]):int(o[i + 1])]),
+                            list(range(b, e)))
