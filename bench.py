@@ -18,7 +18,9 @@ the restore-and-consume step instead: cg_decode_paged of every chunk into a
 paged pool, then cg_attend_paged of one new token per layer over it;
 --level-mix encodes every chunk at the three quality presets and times
 cg_decode of a seeded per-chunk level mix (with --config long: the
-80K-token multi-level workload).
+80K-token multi-level workload); --stream times the streaming workload
+(records from pinned host memory into a paged cache, beside a plain pinned
+copy of the same bytes).
 """
 from __future__ import annotations
 
@@ -27,6 +29,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -39,35 +43,73 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(cfg, X, seconds=10.0, dtype=0, flags=0):
-    """The oracle (single thread) on a bounded sample of the same workload:
-    layer 0, all heads, the first two chunks; build + encode + decode.
-    X: element bits (uint16) of the workload."""
-    import numpy as np
+def host_info():
+    """The host's CPU model and core counts (the oracle baseline's cores)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"cpu": model, "nproc": os.cpu_count(), "usable": aff}
+
+
+def _oracle_sample(O, cfg, lvd, Xs, T, dtype, flags, layer):
+    """build tables + encode + decode of one layer's sample with the oracle."""
+    shp = O.shape(1, cfg.kv_heads, cfg.head_dim, T, cfg.chunk_tokens, dtype)
+    steps = [lvd.steps[lvd.layer_group[layer]]]
+    blob, _ = O.build_tables(shp, lvd.level_id, [0], steps, Xs, flags=flags)
+    data, offs = O.encode_all(shp, blob, Xs)
+    O.decode_all(shp, blob, data, offs)
+
+
+def cpu_baseline(cfg, X, seconds=10.0, dtype=0, flags=0, cores=16):
+    """The oracle on a bounded sample of the same workload: one layer, all
+    heads, the first two chunks; build + encode + decode. First single-
+    threaded (layer 0, repeated for about `seconds`), then the same function
+    on `cores` threads at once, each on its own layer (independent units; the
+    C oracle runs without the GIL). X: element bits (uint16) of the first
+    `cores` layers of the workload."""
+    from concurrent.futures import ThreadPoolExecutor
 
     from oracle import oracle as O
 
     lvd = cfg.levels[0]
     T = min(cfg.tokens, 2 * cfg.chunk_tokens)
-    Xs = np.ascontiguousarray(X[:1, :, :, :T, :])
-    shp = O.shape(1, cfg.kv_heads, cfg.head_dim, T, cfg.chunk_tokens, dtype)
-    steps = [lvd.steps[lvd.layer_group[0]]]
+    samples = [np.ascontiguousarray(X[l:l + 1, :, :, :T, :]) for l in range(X.shape[0])]
     elems = 0
     t0 = time.perf_counter()
     reps = 0
     while True:
-        blob, _ = O.build_tables(shp, lvd.level_id, [0], steps, Xs, flags=flags)
-        data, offs = O.encode_all(shp, blob, Xs)
-        O.decode_all(shp, blob, data, offs)
-        elems += Xs.size
+        _oracle_sample(O, cfg, lvd, samples[0], T, dtype, flags, 0)
+        elems += samples[0].size
         reps += 1
         if time.perf_counter() - t0 >= seconds or reps >= 50:
             break
     dt = time.perf_counter() - t0
+    n = min(cores, len(samples))
+    reps_n = max(1, reps // 2)
+
+    def worker(l):
+        for _ in range(reps_n):
+            _oracle_sample(O, cfg, lvd, samples[l], T, dtype, flags, l)
+
+    t1 = time.perf_counter()
+    with ThreadPoolExecutor(n) as ex:
+        list(ex.map(worker, range(n)))
+    dt_n = time.perf_counter() - t1
     return {"value": round(2 * elems / dt / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": "layer 0 of the workload, %d tokens (%d chunks), all heads: build tables + "
                       "encode + decode, %d repetition(s), %.1f s single-threaded" % (
-                          T, -(-T // cfg.chunk_tokens), reps, dt)}
+                          T, -(-T // cfg.chunk_tokens), reps, dt),
+            "host": host_info(),
+            "x_cores": {"value": round(2 * n * reps_n * samples[0].size / dt_n / 1e9, 5), "unit": "GB/s",
+                        "cores": n, "sample": "the same function on %d threads at once, thread k on layer k "
+                        "(%d repetition(s) each), %.1f s" % (n, reps_n, dt_n)}}
 
 
 def main():
@@ -87,6 +129,9 @@ def main():
                     help="time decode into a paged pool + attention over it")
     ap.add_argument("--level-mix", action="store_true",
                     help="time a decode of chunk records of three quality levels mixed per chunk")
+    ap.add_argument("--stream", action="store_true",
+                    help="the streaming workload: records from pinned host memory decoded into a paged "
+                         "cache while the next one is copied, against a plain pinned copy of the same bytes")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed steps, one library copy of this many bytes (the calibration "
                          "launch for the FETCH_SIZE / WRITE_SIZE counter runs)")
@@ -104,6 +149,8 @@ def main():
 
     C.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.stream:
+        return run_stream(args)
     cfg = synth.CONFIGS[args.config]
     lvd = cfg.levels[0]
     t_gen = time.perf_counter()
@@ -172,6 +219,11 @@ def main():
     wall = time.perf_counter() - t0
     st = cd.read_status()
     assert st == 0, "codec reported status %d" % st
+    # the data's counters (saturated, NaN, escapes) from one more, untimed
+    # table build: asking for them selects the counting variant of k_hist
+    stats = torch.zeros(4, dtype=torch.int64, device=dev)
+    cd_tab.build_tables(x_tab, lv, flags=flags, stats=stats)
+    torch.cuda.synchronize()
     # achievable HBM bandwidth on this machine: the library's copy kernel over
     # 4 GiB (2 x 4 GiB of traffic), best of 3 (skipped in counter-calibration
     # runs, whose only copy launch is the calibration one)
@@ -220,12 +272,14 @@ def main():
     assert bad == 0, "decoded values differ from the reference reconstruction"
 
     # dominant kernel of the step and its roofline
-    n_tables = 2 * lv.n_groups * cfg.kv_heads * cfg.head_dim
-    dec_tables = n_tables * 2048
+    # algorithmic bytes: the table build reads the cache and writes the
+    # tables' format section (512 B per table); the encoder reads the cache
+    # and writes the records; the decoder reads the records and the tables
+    # and writes the cache
     phases = {
         "k_hist": (kms["build"], 2 * x_tab.numel() + fmt),
         "k_encode": (kms["encode"], fp16_bytes + comp),
-        "k_decode": (kms["decode"], fp16_bytes + comp + dec_tables),
+        "k_decode": (kms["decode"], fp16_bytes + comp + fmt),
     }
     dom = max(phases, key=lambda k: phases[k][0])
     variant = args.config + ("-bf16" if bf else "") + ("-robust" if args.robust else "")
@@ -235,7 +289,9 @@ def main():
         gbps = b / (t / 1e3) / 1e9
         r = {"kernel": name, "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
              "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-             "algorithmic_bytes": int(b), "avg_ms": round(float(t), 4)}
+             "algorithmic_bytes": int(b), "avg_ms": round(float(t), 4),
+             "avg_ms_from": "HIP events on the call's stream around each timed launch",
+             "frac_fp16_only": round(fp16_bytes / (t / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
         # counters taken on these very kernel sources and this workload only
         try:
             with open(args.traffic) as f:
@@ -295,6 +351,12 @@ def main():
         "compression_ratio": round(ratio, 3),
         "compressed_fraction": round(comp / fp16_bytes, 4),
         "ratio_incl_tables": round(fp16_bytes / (comp + fmt), 3),
+        "counts": dict(zip(("elements", "saturated", "nan", "escapes"), (int(v) for v in stats.cpu()))),
+        # a monitored figure with the pages' health threshold ("CacheGen实战"
+        # 3.3: compression ratio above 3:1); the decode's share of the restore
+        # latency (under 10 %) is a figure of the streaming line (--stream)
+        "monitor": {"compression_ratio": round(ratio, 3), "ratio_healthy_above": 3.0,
+                    "decode_share_of_round_trip": round(float(t_dec) / (wall / args.steps * 1e3), 4)},
         "roofline": roof(dom),
         "roofline_decode": roof("k_decode"),
         "roofline_alu": roof_alu(dom),
@@ -306,8 +368,138 @@ def main():
         if copy_gbps else None,
     }
     if not args.no_cpu_baseline:
-        xb = x[:1].cpu().view(torch.int16).numpy().view(np.uint16)
-        res["cpu_baseline"] = cpu_baseline(cfg, xb, args.cpu_seconds, dt, flags)
+        ncores = min(16, host_info()["usable"] or 1, cfg.layers)
+        xb = x[:ncores, :, :, :2 * cfg.chunk_tokens].cpu().view(torch.int16).numpy().view(np.uint16)
+        res["cpu_baseline"] = cpu_baseline(cfg, xb, args.cpu_seconds, dt, flags, cores=ncores)
+    print(json.dumps(res), flush=True)
+
+
+def run_stream(args):
+    """The streaming workload ("CacheGen实战" 2.3: a receive stage, parallel
+    GPU decode and a fill stage as a pipeline): the 16K-token 7B-shape cache
+    with Student-t innovations is encoded, its 11 records are put in pinned
+    host memory, and cg_stream_decode_paged copies each record to the GPU on
+    a second stream while the previous one decodes into 16-token pages
+    through a seeded random block table. Beside it: a plain pinned
+    host-to-device copy of the same bytes (the bound of the pipeline) and the
+    decode kernels alone, one record per launch as the pipeline issues them.
+    step = one streamed restore of the whole cache; value = restored fp16
+    bytes per second."""
+    import torch
+
+    from kv_cache_compression_encode_amd import cg as C
+    from kv_cache_compression_encode_amd import codec, synth
+
+    cfg = synth.CONFIGS["stream"]
+    lvd = cfg.levels[0]
+    X = synth.generate(cfg)
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.float16)
+    shp = codec.shape_of(cfg)
+    lv = codec.level_of(lvd)
+    cd = codec.Codec(shp, dev)
+    stats = torch.zeros(4, dtype=torch.int64, device=dev)
+    tables = cd.build_tables(x, lv, stats=stats)
+    out, offs = cd.encode(x, lv, tables)
+    assert cd.read_status() == 0
+    fp16_bytes = 2 * x.numel()
+    del x
+    o = offs.cpu().numpy().astype(np.uint64)
+    n = len(o) - 1
+    rec_bytes = int(o[-1])
+    host = torch.empty(rec_bytes, dtype=torch.uint8).pin_memory()
+    host.copy_(out[:rec_bytes].cpu())
+    bt = synth.block_table(cfg)
+    NB = len(bt)
+    btd = torch.from_numpy(bt).to(dev)
+    pool = torch.empty((cfg.layers, 2, NB, cfg.kv_heads, 16, cfg.head_dim), dtype=torch.float16, device=dev)
+    staging = torch.empty(2 * int(np.diff(o).max()) + 512, dtype=torch.uint8, device=dev)
+    refs2 = torch.empty(2 * C.REF_BYTES, dtype=torch.uint8, device=dev)
+    copy_stream = torch.cuda.Stream()
+    stream = torch.cuda.current_stream()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # the bound: one plain pinned host-to-device copy of all record bytes
+    dst = torch.empty(rec_bytes, dtype=torch.uint8, device=dev)
+    copy_ms = []
+    for _ in range(3):
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        dst.copy_(host, non_blocking=True)
+        e1.record(stream)
+        e1.synchronize()
+        copy_ms.append(e0.elapsed_time(e1))
+    del dst
+    h2d_gbps = rec_bytes / (min(copy_ms) / 1e3) / 1e9
+
+    def streamed():
+        C.cg_stream_decode_paged(cd.shp, [lv], [tables], host, o, None, n, staging, refs2, pool, NB, btd,
+                                 cd.status, copy_stream=copy_stream)
+
+    for _ in range(args.warmup):
+        streamed()
+    torch.cuda.synchronize()
+    assert cd.read_status() == 0
+    evs = [(ev(), ev()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        streamed()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert cd.read_status() == 0
+    step_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    # the decode kernels alone, one record per launch as the pipeline issues them
+    dec_ms = []
+    for k in range(n):
+        refs, _ = cd.make_refs([(out, offs, [k], 0)])
+        kt = C.KernelTimer()
+        cd.decode_paged([lv], [tables], refs, 1, pool, btd, prof=kt)
+        torch.cuda.synchronize()
+        dec_ms.append(kt.elapsed_ms())
+    assert cd.read_status() == 0
+    ratio = fp16_bytes / rec_bytes
+    res = {
+        "metric": METRIC,
+        "value": round(fp16_bytes / (wall / args.steps) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 data; fp32 dequantize, u32 rANS",
+        "data": "synthetic",
+        "config": {"workload": "stream: %d layers x %d KV heads x %d dim x %d tokens, fp16 K+V, Student-t(3) "
+                               "innovations, chunk %d, %s steps %s; %d records streamed from pinned host memory "
+                               "into 16-token pages of a seeded random block table" % (
+                                   cfg.layers, cfg.kv_heads, cfg.head_dim, cfg.tokens, cfg.chunk_tokens,
+                                   lvd.name, "/".join(str(v) for v in lvd.steps), n),
+                   "fp16_bytes": fp16_bytes, "record_bytes": rec_bytes, "records": n},
+        "stream_ms": round(step_ms, 3),
+        "records_GBps": round(rec_bytes / (step_ms / 1e3) / 1e9, 2),
+        "h2d_copy_GBps": round(h2d_gbps, 2),
+        "frac_of_h2d_copy": round(rec_bytes / (step_ms / 1e3) / 1e9 / h2d_gbps, 4),
+        "decode_kernels_ms": round(float(np.sum(dec_ms)), 3),
+        "compression_ratio": round(ratio, 3),
+        "counts": dict(zip(("elements", "saturated", "nan", "escapes"), (int(v) for v in stats.cpu()))),
+        # the pages' monitored figures ("CacheGen实战" 3.3): decode latency
+        # under 10 % of the total, compression ratio above 3:1. The decode
+        # runs under the next record's copy, so the latency it adds to the
+        # restore is the streamed time beyond a plain copy of the same bytes;
+        # the kernels' own time is given beside it
+        "monitor": {"compression_ratio": round(ratio, 3), "ratio_healthy_above": 3.0,
+                    "decode_latency_share": round(max(0.0, step_ms - rec_bytes / h2d_gbps / 1e6) / step_ms, 4),
+                    "decode_share_healthy_below": 0.10,
+                    "decode_kernels_share": round(float(np.sum(dec_ms)) / step_ms, 4)},
+    }
     print(json.dumps(res), flush=True)
 
 

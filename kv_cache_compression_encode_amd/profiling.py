@@ -59,6 +59,30 @@ def kernel_stats(run_dir: str):
     return rows
 
 
+def kernel_trace(run_dir: str):
+    """Kernel name -> durations in microseconds, in dispatch order, from
+    *_kernel_trace.csv."""
+    per = {}
+    with open(_one(os.path.join(run_dir, "**", "*kernel_trace.csv"))) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+    for r in rows:
+        per.setdefault(r["Kernel_Name"], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return per
+
+
+def timed_average(run_dir: str, skip: int):
+    """Short kernel name -> (launches, mean us) over each codec kernel's
+    launches after its first `skip` (the benchmark's warm-up steps)."""
+    out = {}
+    for name, d in kernel_trace(run_dir).items():
+        for short, frag in KERNELS.items():
+            if frag in name and len(d) > skip:
+                t = d[skip:]
+                out[short] = (len(t), sum(t) / len(t))
+    return out
+
+
 def counter_per_kernel(run_dir: str, counter: str):
     """short kernel name -> mean counter value per dispatch (KiB for the
     size counters), from *_counter_collection.csv."""
@@ -148,6 +172,10 @@ def main():
     s.add_argument("--title", required=True)
     s.add_argument("--command", required=True, help="the command that produced run_dir")
     s.add_argument("--note", default="")
+    s.add_argument("--skip", type=int, default=0,
+                   help="warm-up launches per codec kernel left out of the timed-launch averages")
+    s.add_argument("--bench-json", default="",
+                   help="the JSON line bench.py printed in the same run (its event-timed kernel averages)")
     s.add_argument("--out", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True, help="output dir of the FETCH_SIZE run")
@@ -235,6 +263,24 @@ def main():
             f.write("| kernel | calls | average us | total ms | % |\n|---|---|---|---|---|\n")
             for name, calls, avg, tot, pct in rows:
                 f.write("| `%s` | %d | %.1f | %.2f | %.2f |\n" % (name[:90], calls, avg, tot, pct))
+            if a.skip:
+                ta = timed_average(a.run_dir, a.skip)
+                bench = {}
+                if a.bench_json:
+                    with open(a.bench_json) as bj:
+                        line = [ln for ln in bj.read().splitlines() if ln.startswith("{")][-1]
+                    bench = json.loads(line).get("kernel_ms", {})
+                f.write("\nTimed launches only (each codec kernel's first %d launches, the warm-up steps, left "
+                        "out), from the per-dispatch trace%s:\n\n" % (
+                            a.skip, ", beside the HIP-event averages bench.py printed in the same run"
+                            if bench else ""))
+                f.write("| kernel | timed launches | trace average us | bench.py events us | trace / events |\n"
+                        "|---|---|---|---|---|\n")
+                for k, (nl, us) in sorted(ta.items()):
+                    ev = bench.get(k)
+                    f.write("| %s | %d | %.1f | %s | %s |\n" % (
+                        k, nl, us, "%.1f" % (1e3 * ev) if ev else "-",
+                        "%.3f" % (us / (1e3 * ev)) if ev else "-"))
         print("wrote", a.out)
     else:
         tr = traffic(a.fetch, a.write, a.copy_bytes)
