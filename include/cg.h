@@ -151,6 +151,22 @@ cg_status cg_build_tables(const cg_shape* shape, const cg_level* level, const ui
                           void* tables_dev, void* ws_dev, size_t ws_bytes, uint32_t flags,
                           uint64_t* stats_dev, const cg_profile* prof, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): as
+ * cg_build_tables, but the symbol counts live in a static device array of
+ * CG_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends, so no workspace argument is needed and the call
+ * allocates nothing. Returns CG_ERR_UNSUPPORTED when the counts
+ * (cg_build_workspace_bytes) exceed that size (a 7B-shape level of three
+ * layer groups needs 25.2 MB), CG_ERR_HIP if the array's address cannot be
+ * found. Every call on one GPU shares that GPU's array: calls that overlap
+ * in time on one GPU (other streams, other threads) race; the array is
+ * cleared at the start of each call. */
+#define CG_NOALLOC_SCRATCH_BYTES (32u << 20)
+cg_status cg_build_tables_noalloc(const cg_shape* shape, const cg_level* level, const uint16_t* x_dev,
+                                  void* tables_dev, uint32_t flags, uint64_t* stats_dev,
+                                  const cg_profile* prof, hipStream_t stream);
+
 /* ---- encode -------------------------------------------------------------- */
 
 /* Worst-case bytes of the records of chunks [chunk_begin, chunk_end). */

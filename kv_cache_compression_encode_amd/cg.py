@@ -23,6 +23,7 @@ CG_ERR_TABLE = -6
 CG_DTYPE_F16 = 0
 CG_DTYPE_BF16 = 1
 CG_TABLES_ROBUST = 1
+CG_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class CgError(RuntimeError):
@@ -132,6 +133,7 @@ def lib():
         "cg_tables_format_bytes": (sz, [sp, i32]),
         "cg_build_workspace_bytes": (sz, [sp, i32]),
         "cg_build_tables": (i32, [sp, lp, P, P, P, sz, ctypes.c_uint32, P, pp, P]),
+        "cg_build_tables_noalloc": (i32, [sp, lp, P, P, ctypes.c_uint32, P, pp, P]),
         "cg_encode_bound": (sz, [sp, i64, i64]),
         "cg_encode_workspace_bytes": (sz, [sp, i64, i64]),
         "cg_encode": (i32, [sp, lp, P, P, i64, i64, P, u64, P, P, sz, P, pp, P]),
@@ -155,7 +157,7 @@ def lib():
 
 
 EXPORTS = ("cg_version", "cg_status_string", "cg_tables_bytes", "cg_tables_format_bytes",
-           "cg_build_workspace_bytes", "cg_build_tables", "cg_encode_bound",
+           "cg_build_workspace_bytes", "cg_build_tables", "cg_build_tables_noalloc", "cg_encode_bound",
            "cg_encode_workspace_bytes", "cg_encode", "cg_make_refs", "cg_decode",
            "cg_decode_paged", "cg_decode_plan", "cg_stream_decode_paged", "cg_copy", "cg_select_level",
            "cg_recency_levels", "cg_attend_workspace_bytes", "cg_attend_paged")
@@ -216,6 +218,12 @@ def cg_build_tables(shp, level: Level, x, tables, ws, flags=0, stats=None, prof=
                                _ptr(ws), ws.numel() * ws.element_size(), int(flags), _ptr(stats),
                                _prof(prof), _stream(stream))
     _check("cg_build_tables", rc)
+
+
+def cg_build_tables_noalloc(shp, level: Level, x, tables, flags=0, stats=None, prof=None, stream=None):
+    rc = lib().cg_build_tables_noalloc(ctypes.byref(shp), ctypes.byref(level.c), _ptr(x), _ptr(tables),
+                                       int(flags), _ptr(stats), _prof(prof), _stream(stream))
+    _check("cg_build_tables_noalloc", rc)
 
 
 def cg_encode_bound(shp, chunk_begin, chunk_end) -> int:

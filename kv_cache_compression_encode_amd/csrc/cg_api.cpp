@@ -8,6 +8,7 @@
 #include <cstring>
 #include <algorithm>
 #include <functional>
+#include <mutex>
 #include <utility>
 #include <vector>
 
@@ -271,6 +272,35 @@ size_t cg_tables_format_bytes(const cg_shape* shape, int32_t n_groups) {
   return (size_t)tb_format_bytes(s.L, s.H, s.D, n_groups);
 }
 
+// ---- scratch of the allocation-free table build -----------------------------
+// cg_build_tables_noalloc keeps the symbol counts in this file-scope device
+// array instead of a caller workspace. Each GPU the library runs on holds its
+// own copy until the process ends. In host code the name `scratch` is only a
+// stand-in: its device address on each GPU comes from hipGetSymbolAddress
+// (scratch_address below), and only that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[CG_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];  // per device: the array's device address
+
+// The array's address on the current device, looked up on the first call
+// on that device (with it current) and kept.
+cg_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CG_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CG_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return CG_OK;
+}
+}  // namespace
+
 size_t cg_build_workspace_bytes(const cg_shape* shape, int32_t n_groups) {
   Shape s;
   if (check_shape(shape, &s) != CG_OK || n_groups < 1 || n_groups > kMaxGroups) return 0;
@@ -345,6 +375,23 @@ cg_status cg_build_tables(const cg_shape* shape, const cg_level* level, const ui
   na.n_tables = (int64_t)ntab;
   na.robust = (flags & CG_TABLES_ROBUST) != 0;
   return hip_status(launch_norm(na, stream));
+}
+
+cg_status cg_build_tables_noalloc(const cg_shape* shape, const cg_level* level, const uint16_t* x_dev,
+                                  void* tables_dev, uint32_t flags, uint64_t* stats_dev,
+                                  const cg_profile* prof, hipStream_t stream) {
+  Shape s;
+  cg_status rc = check_shape(shape, &s);
+  if (rc != CG_OK) return rc;
+  if ((rc = check_level(level, s)) != CG_OK) return rc;
+  const size_t need = cg_build_workspace_bytes(shape, level->n_groups);
+  if (need == 0) return CG_ERR_INVALID_ARG;
+  if (need > CG_NOALLOC_SCRATCH_BYTES) return CG_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws)) != CG_OK) return rc;
+  // the counts are cleared by cg_build_tables' own fill kernel
+  return cg_build_tables(shape, level, x_dev, tables_dev, ws, CG_NOALLOC_SCRATCH_BYTES, flags, stats_dev, prof,
+                         stream);
 }
 
 size_t cg_encode_bound(const cg_shape* shape, int64_t chunk_begin, int64_t chunk_end) {
