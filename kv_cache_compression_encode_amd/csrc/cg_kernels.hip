@@ -622,12 +622,16 @@ __global__ void __launch_bounds__(kNormThreads) k_norm(NormArgs a) {
   // encoder set: f | b << 16 | escape << 31 per symbol. The escape
   // symbol's entry carries the flag; with robust tables a symbol of
   // frequency 0 gets the escape's entry, so the encoder escapes it.
+  // Without, such a symbol gets the flag with f = 0: the encoder's escape
+  // branch (the only place it looks) reports an escaping lane whose entry
+  // has f = 0, which also covers an escape symbol of frequency 0.
   uint32_t* enc = reinterpret_cast<uint32_t*>(a.blob + a.enc_off) + set * (kEncDwords * 64) + kk;
   const uint32_t esc_entry = __shfl(f[3] | (b[3] << 16), 63) | 0x80000000u;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     uint32_t e = f[k] | (b[k] << 16);
-    if (4 * lane + k == 255 || (a.robust && f[k] == 0)) e = esc_entry;
+    if (4 * lane + k == 255) e = esc_entry;
+    else if (f[k] == 0) e = a.robust ? esc_entry : (esc_entry & 0xFFFF0000u);
     enc[(4 * lane + k) * 64] = e;
   }
   // decoder set: reversed start bitmap, scaled rank bases, rank -> (d, 4096-f, b)
@@ -713,18 +717,24 @@ __device__ __forceinline__ void enc_s1(EncTok& k, uint16_t xprev, int32_t& qhi, 
 
 // the escape decision comes from the entry: symbol 255 (a wide delta) and,
 // with robust tables, every symbol of frequency 0 carry the flag
-__device__ __forceinline__ void enc_s2(EncTok& k, const double* rcp_tab, uint32_t& fmin) {
+__device__ __forceinline__ void enc_s2(EncTok& k, const double* rcp_tab) {
   k.esc = (int32_t)k.e < 0;
   k.me = __ballot(k.esc);
   k.f = k.e & 0xFFFFu;
-  fmin = k.f < fmin ? k.f : fmin;
   k.r = rcp_tab[k.f];
 }
 
-__device__ __forceinline__ void enc_s3(const EncTok& k, uint32_t& x, uint32_t& P, __amdgpu_buffer_rsrc_t sr) {
+// Every entry of frequency 0 carries the escape flag (see k_norm), so an
+// escaping lane with f = 0 is the only way a symbol missing from the table
+// shows; the table is then invalid and the call reports CG_ERR_TABLE.
+// (reported from inside the branch: a flag carried to the end of the group
+// would be updated by a select on every token)
+__device__ __forceinline__ void enc_s3(const EncTok& k, uint32_t& x, uint32_t& P, __amdgpu_buffer_rsrc_t sr,
+                                       int32_t* status, int lane) {
   if (k.me) {
     P -= (uint32_t)__popcll(k.me);
     if (k.esc) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)k.d16, sr, 2u * mbcnt_base(k.me, 0), 2u * P, 0);
+    if (__builtin_expect(__ballot(k.esc && k.f == 0) != 0, 0) && lane == 0) set_status(status, CG_ERR_TABLE);
   }
   // renormalise when x >= f * 2^20, i.e. floor(x / 2^20) >= f (never for f = 4096)
   const uint64_t mr = __ballot((x >> 20) >= k.f);
@@ -746,12 +756,11 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
                                              float step, float rcp, const uint32_t* ftab,
                                              const double* rcp_tab, __amdgpu_buffer_rsrc_t sr,
                                              uint32_t cap, int lane, uint32_t& words,
-                                             uint32_t& start, bool& table_err, int* left, int wave,
+                                             uint32_t& start, int32_t* status, int* left, int wave,
                                              int left_after) {
   const uint32_t lane2 = 2u * lane;
   uint32_t P = cap;
   uint32_t x = kL;
-  uint32_t fmin = 0xFFFFFFFFu;
   auto row = [&](int r) { return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, (uint32_t)r * row_bytes, 0); };
   uint32_t d0 = 0, d1 = 0;
   int32_t qhi = quantize<QM, BF>(row(n - 1), step, rcp, d0, d1);
@@ -760,59 +769,87 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
     // S2, token n-2 through S1.
     EncTok a, b, c;
     enc_s1<QM, BF>(a, row(n - 2), qhi, step, rcp, ftab, lane);
-    enc_s2(a, rcp_tab, fmin);
+    enc_s2(a, rcp_tab);
     enc_s1<QM, BF>(b, row(n - 3), qhi, step, rcp, ftab, lane);
     // tokens i, i-1, ... enter S1 with x of rows i-1, i-2, ...; the rows of
     // the next batch are loaded while the current one is encoded. Offsets
     // stay scalar: a batch of 16 rows all >= 0 needs no clamp; the last one
     // clamps at 0. (32-bit slots, as in hist_range)
-    auto load_batch = [&](uint32_t* v, int i0) {
-      if (i0 >= kEncBatch) {
-        const uint32_t o0 = (uint32_t)(i0 - 1) * row_bytes;
+    // rows i0 - 1, ..., i0 - 16 (i0 >= 16: all of them exist)
+    auto load_rows = [&](uint32_t* v, int i0) {
+      const uint32_t o0 = (uint32_t)(i0 - 1) * row_bytes;
 #pragma unroll
-        for (int k = 0; k < kEncBatch; ++k)
-          v[k] = __builtin_amdgcn_raw_buffer_load_b16(xr, lane2, o0 - (uint32_t)k * row_bytes, 0);
-      } else {
+      for (int k = 0; k < kEncBatch; ++k)
+        v[k] = __builtin_amdgcn_raw_buffer_load_b16(xr, lane2, o0 - (uint32_t)k * row_bytes, 0);
+    };
+    // the same rows, those below 0 replaced by row 0 (any i0)
+    auto load_rows_clamped = [&](uint32_t* v, int i0) {
 #pragma unroll
-        for (int k = 0; k < kEncBatch; ++k) {
-          const int r = i0 - 1 - k > 0 ? i0 - 1 - k : 0;
-          v[k] = __builtin_amdgcn_raw_buffer_load_b16(xr, lane2, uni((uint32_t)r * row_bytes), 0);
-        }
+      for (int k = 0; k < kEncBatch; ++k) {
+        const int r = i0 - 1 - k > 0 ? i0 - 1 - k : 0;
+        v[k] = __builtin_amdgcn_raw_buffer_load_b16(xr, lane2, uni((uint32_t)r * row_bytes), 0);
       }
     };
     int i = n - 3;  // next token to enter S1
-    uint32_t xv[kEncBatch];
-    load_batch(xv, i);
+    // Three batches of rows in flight: the batch a step encodes was loaded
+    // two steps earlier. The renormalisation stores are inline assembly the
+    // compiler does not count, so the vmcnt wait it places before a row's
+    // first use also covers every operation issued after that row's load
+    // beyond the loads it knows of; with the batch loaded one step ahead that
+    // wait reached the loads just issued (or, before them, the stores just
+    // issued) and exposed a memory round trip every 16 tokens.
+    uint32_t xa[kEncBatch], xb[kEncBatch], xc[kEncBatch];
+    load_rows_clamped(xa, i);
+    load_rows_clamped(xb, i - kEncBatch);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // as in hist_range
     auto advance = [&](uint16_t xprev) {
       enc_s1<QM, BF>(c, xprev, qhi, step, rcp, ftab, lane);
-      enc_s2(b, rcp_tab, fmin);
-      enc_s3(a, x, P, sr);
+      enc_s2(b, rcp_tab);
+      enc_s3(a, x, P, sr, status, lane);
       a = b;
       b = c;
     };
     static_assert(2 * kEncBatch == kProgressPeriod, "progress every second batch");
+    // one step: encode the batch of tokens at, ..., at - 15 and load the
+    // batch two ahead; three steps per iteration, rotating the registers.
+    // The loop runs while every row it loads exists (at - 32 >= 16), so its
+    // loads need no clamp: a clamped variant on one of two paths put a
+    // register copy, and a full vmcnt wait, on both.
+    auto step16 = [&](uint32_t* cur, uint32_t* ahead, int at) {
+      if (at & kEncBatch) publish_progress<kWaves>(left, wave, left_after + at, lane);
+      load_rows(ahead, at - 2 * kEncBatch);
+#pragma unroll
+      for (int k = 0; k < kEncBatch; ++k) advance((uint16_t)cur[k]);
+    };
+    for (; i >= 5 * kEncBatch; i -= 3 * kEncBatch) {
+      step16(xa, xc, i);
+      step16(xb, xa, i - kEncBatch);
+      step16(xc, xb, i - 2 * kEncBatch);
+    }
+    // the last batches (at most four), rows moved once per batch
     for (; i >= kEncBatch; i -= kEncBatch) {
       if (i & kEncBatch) publish_progress<kWaves>(left, wave, left_after + i, lane);
-      uint32_t xn[kEncBatch];
-      load_batch(xn, i - kEncBatch);
+      load_rows_clamped(xc, i - 2 * kEncBatch);
 #pragma unroll
-      for (int k = 0; k < kEncBatch; ++k) advance((uint16_t)xv[k]);
+      for (int k = 0; k < kEncBatch; ++k) advance((uint16_t)xa[k]);
 #pragma unroll
-      for (int k = 0; k < kEncBatch; ++k) xv[k] = xn[k];
+      for (int k = 0; k < kEncBatch; ++k) {
+        xa[k] = xb[k];
+        xb[k] = xc[k];
+      }
     }
 #pragma unroll
     for (int k = 0; k < kEncBatch; ++k)  // the last i < 16 tokens
-      if (k < i) advance((uint16_t)xv[k]);
+      if (k < i) advance((uint16_t)xa[k]);
     // epilogue: the last two tokens leave the pipeline
-    enc_s2(b, rcp_tab, fmin);
-    enc_s3(a, x, P, sr);
-    enc_s3(b, x, P, sr);
+    enc_s2(b, rcp_tab);
+    enc_s3(a, x, P, sr, status, lane);
+    enc_s3(b, x, P, sr, status, lane);
   } else if (n == 2) {
     EncTok a;
     enc_s1<QM, BF>(a, row(0), qhi, step, rcp, ftab, lane);
-    enc_s2(a, rcp_tab, fmin);
-    enc_s3(a, x, P, sr);
+    enc_s2(a, rcp_tab);
+    enc_s3(a, x, P, sr, status, lane);
   }
   P -= 64;
   __builtin_amdgcn_raw_buffer_store_b16((uint16_t)qhi, sr, lane2, 2u * P, 0);
@@ -822,7 +859,6 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
   __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(x >> 16), sr, lane2, 2u * P, 0);
   words = cap - P;
   start = P;
-  table_err |= (fmin == 0);
 }
 
 // The k-th layer (0-based, ascending) of layer group g, or -1; computed by
@@ -906,7 +942,6 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
   const int qm = qmode(a.blob, s.L, s.H, s.D, G, g);
   const int64_t gpc = groups_per_chunk(s.L, s.H, s.D);
   const uint32_t cap = (uint32_t)a.cap_words;
-  bool table_err = false;
   // items = (chunk, k-th layer of the group), chunk-major; wavefront w takes
   // items w, w + 16, ...
   const int lg_count = layers_in_group(a.blob, G, s.L, g, lane);
@@ -928,7 +963,7 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(xb, (uint32_t)n * row_bytes);
     uint32_t words, start;
 #define CG_ENC(QM) \
-  encode_group<QM, BF>(xr, (int)n, row_bytes, step, rcp, ftab, rcp_tab, sr, cap, lane, words, start, table_err, \
+  encode_group<QM, BF>(xr, (int)n, row_bytes, step, rcp, ftab, rcp_tab, sr, cap, lane, words, start, a.status, \
                left, wave, my_left)
     if (qm == kQuotMul) CG_ENC(kQuotMul);
     else if (qm == kQuotFma) CG_ENC(kQuotFma);
@@ -940,7 +975,6 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
     }
   }
   if (lane == 0) left[wave] = 0;
-  if (__ballot(table_err) && lane == 0) set_status(a.status, CG_ERR_TABLE);
 }
 
 // ---------------------------------------------------------------------------
