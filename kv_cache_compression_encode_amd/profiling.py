@@ -71,14 +71,16 @@ def kernel_trace(run_dir: str):
     return per
 
 
-def timed_average(run_dir: str, skip: int):
+def timed_average(run_dir: str, skip: int, count: int = 0):
     """Short kernel name -> (launches, mean us) over each codec kernel's
-    launches after its first `skip` (the benchmark's warm-up steps)."""
+    launches after its first `skip` (the benchmark's warm-up steps); with
+    count > 0 only the `count` launches after those (the timed steps, not an
+    untimed launch the benchmark makes afterwards)."""
     out = {}
     for name, d in kernel_trace(run_dir).items():
         for short, frag in KERNELS.items():
             if frag in name and len(d) > skip:
-                t = d[skip:]
+                t = d[skip:skip + count] if count > 0 else d[skip:]
                 out[short] = (len(t), sum(t) / len(t))
     return out
 
@@ -264,15 +266,18 @@ def main():
             for name, calls, avg, tot, pct in rows:
                 f.write("| `%s` | %d | %.1f | %.2f | %.2f |\n" % (name[:90], calls, avg, tot, pct))
             if a.skip:
-                ta = timed_average(a.run_dir, a.skip)
-                bench = {}
+                bench, steps = {}, 0
                 if a.bench_json:
                     with open(a.bench_json) as bj:
                         line = [ln for ln in bj.read().splitlines() if ln.startswith("{")][-1]
-                    bench = json.loads(line).get("kernel_ms", {})
+                    bj_doc = json.loads(line)
+                    bench = bj_doc.get("kernel_ms", {})
+                    steps = int(bj_doc.get("steps", 0))
+                ta = timed_average(a.run_dir, a.skip, steps)
                 f.write("\nTimed launches only (each codec kernel's first %d launches, the warm-up steps, left "
-                        "out), from the per-dispatch trace%s:\n\n" % (
-                            a.skip, ", beside the HIP-event averages bench.py printed in the same run"
+                        "out%s), from the per-dispatch trace%s:\n\n" % (
+                            a.skip, ", and only the next %d, the timed steps" % steps if steps else "",
+                            ", beside the HIP-event averages bench.py printed in the same run"
                             if bench else ""))
                 f.write("| kernel | timed launches | trace average us | bench.py events us | trace / events |\n"
                         "|---|---|---|---|---|\n")
