@@ -120,13 +120,13 @@ __device__ __forceinline__ int32_t quantize(uint16_t xh, float step, float rcp, 
   if (QM == kQuotMul) {
     v = x * rcp;  // NaN stays NaN, Inf and overflow saturate below
   } else if (QM == kQuotFma) {
-    const float v1 = x * rcp;
+    // x*r clamped to +-65536 first, so the correction is finite unless x
+    // is NaN (then NaN -> 0, as the quotient): a finite x beyond the clamp
+    // (bfloat16 reaches 3.4e38) or an infinite one lands beyond +-32767.5
+    // and saturates as the quotient does; inside it nothing changes
+    const float v1 = __builtin_amdgcn_fmed3f(x * rcp, -65536.0f, 65536.0f);
     const float e = __builtin_fmaf(-v1, step, x);
-    const float v2 = __builtin_fmaf(e, rcp, v1);
-    // v2 is NaN when x*r is not finite: x is Inf or NaN, or a finite x
-    // (bfloat16 reaches 3.4e38) overflows x*r; keep x*r, which saturates
-    // or gives NaN -> 0 as the quotient would
-    v = (v2 == v2) ? v2 : v1;
+    v = __builtin_fmaf(e, rcp, v1);
   } else {
     v = x / step;
   }
@@ -625,14 +625,22 @@ __global__ void __launch_bounds__(kNormThreads) k_norm(NormArgs a) {
   // Without, such a symbol gets the flag with f = 0: the encoder's escape
   // branch (the only place it looks) reports an escaping lane whose entry
   // has f = 0, which also covers an escape symbol of frequency 0.
+  // Rows are indexed by delta + 128 (symbol + 1); the escape's entry fills
+  // rows 0 and 256, which the clamped deltas beyond +-127 reach.
   uint32_t* enc = reinterpret_cast<uint32_t*>(a.blob + a.enc_off) + set * (kEncDwords * 64) + kk;
   const uint32_t esc_entry = __shfl(f[3] | (b[3] << 16), 63) | 0x80000000u;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
+    const int sym = 4 * lane + k;
     uint32_t e = f[k] | (b[k] << 16);
-    if (4 * lane + k == 255) e = esc_entry;
+    if (sym == 255) e = esc_entry;
     else if (f[k] == 0) e = a.robust ? esc_entry : (esc_entry & 0xFFFF0000u);
-    enc[(4 * lane + k) * 64] = e;
+    if (sym < 255) {
+      enc[(sym + 1) * 64] = e;
+    } else {
+      enc[0] = e;
+      enc[256 * 64] = e;
+    }
   }
   // decoder set: reversed start bitmap, scaled rank bases, rank -> (d, 4096-f, b)
   uint32_t* dec = reinterpret_cast<uint32_t*>(a.blob + a.dec_off) + set * (kDecDwords * 64) + kk;
@@ -704,14 +712,27 @@ struct EncTok {
   double r;      // RU(1/f) (S2 read)
 };
 
+// q_t - q_{t-1} wrapped to 16 bits and sign-extended, in one instruction
+// (the SDWA form sign-extends its 16-bit result)
+__device__ __forceinline__ int32_t sub_wrap16(int32_t a, int32_t b) {
+  int32_t r;
+  asm("v_sub_u32_sdwa %0, %1, %2 dst_sel:WORD_0 dst_unused:UNUSED_SEXT src0_sel:DWORD src1_sel:DWORD"
+      : "=v"(r)
+      : "v"(a), "v"(b));
+  return r;
+}
+
+// row0: the lane's column of the encoder table at row 128 (delta 0); the
+// entry of delta d is row0[64 * clamp(d, -128, 128)]
 template <int QM, bool BF>
 __device__ __forceinline__ void enc_s1(EncTok& k, uint16_t xprev, int32_t& qhi, float step, float rcp,
-                                       const uint32_t* ftab, int lane) {
+                                       const uint32_t* row0) {
   uint32_t d0 = 0, d1 = 0;
   const int32_t qlo = quantize<QM, BF>(xprev, step, rcp, d0, d1);
-  k.d16 = (uint32_t)(qhi - qlo);
-  const uint32_t sraw = sym_raw(qhi, qlo);
-  k.e = ftab[(sraw < 255u ? sraw : 255u) * 64 + lane];
+  const int32_t d = sub_wrap16(qhi, qlo);
+  k.d16 = (uint32_t)d;
+  const int32_t m = d < -128 ? -128 : (d > 128 ? 128 : d);
+  k.e = row0[m * 64];
   qhi = qlo;
 }
 
@@ -759,6 +780,7 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
                                              uint32_t& start, int32_t* status, int* left, int wave,
                                              int left_after) {
   const uint32_t lane2 = 2u * lane;
+  const uint32_t* row0 = ftab + 128 * 64 + lane;
   uint32_t P = cap;
   uint32_t x = kL;
   auto row = [&](int r) { return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, (uint32_t)r * row_bytes, 0); };
@@ -768,9 +790,9 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
     // a: token in S3, b: in S2, c: in S1. Prologue: token n-1 through S1 and
     // S2, token n-2 through S1.
     EncTok a, b, c;
-    enc_s1<QM, BF>(a, row(n - 2), qhi, step, rcp, ftab, lane);
+    enc_s1<QM, BF>(a, row(n - 2), qhi, step, rcp, row0);
     enc_s2(a, rcp_tab);
-    enc_s1<QM, BF>(b, row(n - 3), qhi, step, rcp, ftab, lane);
+    enc_s1<QM, BF>(b, row(n - 3), qhi, step, rcp, row0);
     // tokens i, i-1, ... enter S1 with x of rows i-1, i-2, ...; the rows of
     // the next batch are loaded while the current one is encoded. Offsets
     // stay scalar: a batch of 16 rows all >= 0 needs no clamp; the last one
@@ -803,7 +825,7 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
     load_rows_clamped(xb, i - kEncBatch);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // as in hist_range
     auto advance = [&](uint16_t xprev) {
-      enc_s1<QM, BF>(c, xprev, qhi, step, rcp, ftab, lane);
+      enc_s1<QM, BF>(c, xprev, qhi, step, rcp, row0);
       enc_s2(b, rcp_tab);
       enc_s3(a, x, P, sr, status, lane);
       a = b;
@@ -847,7 +869,7 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
     enc_s3(b, x, P, sr, status, lane);
   } else if (n == 2) {
     EncTok a;
-    enc_s1<QM, BF>(a, row(0), qhi, step, rcp, ftab, lane);
+    enc_s1<QM, BF>(a, row(0), qhi, step, rcp, row0);
     enc_s2(a, rcp_tab);
     enc_s3(a, x, P, sr, status, lane);
   }
