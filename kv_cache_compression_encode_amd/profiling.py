@@ -86,8 +86,11 @@ def timed_average(run_dir: str, skip: int, count: int = 0):
 
 
 def counter_per_kernel(run_dir: str, counter: str):
-    """short kernel name -> mean counter value per dispatch (KiB for the
-    size counters), from *_counter_collection.csv."""
+    """short kernel name -> counter value of the kernel's first dispatch (KiB
+    for the size counters), from *_counter_collection.csv. The counter runs
+    time one step without warm-up, so the first dispatch of each codec
+    kernel is the step's; a later one is bench.py's untimed counting build
+    (a k_hist variant with more work) or its copy."""
     vals = {}
     with open(_one(os.path.join(run_dir, "**", "*counter_collection.csv"))) as f:
         for r in csv.DictReader(f):
@@ -95,8 +98,8 @@ def counter_per_kernel(run_dir: str, counter: str):
                 continue
             for short, frag in KERNELS.items():
                 if frag in r["Kernel_Name"]:
-                    vals.setdefault(short, []).append(float(r["Counter_Value"]))
-    return {k: sum(v) / len(v) for k, v in vals.items()}
+                    vals.setdefault(short, []).append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    return {k: min(v)[1] for k, v in vals.items()}
 
 
 def traffic(fetch_dir: str, write_dir: str, copy_bytes: int):
@@ -123,15 +126,12 @@ SQ_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", 
 VALU_PEAK_OPS = 256 * 4 * 16 * 2.4e9
 
 
-def sq(sq_dir: str, trace_dir: str):
-    """Per kernel: mean SQ counters per dispatch and, with the kernel-trace
-    average duration, the achieved VALU lane-operation rate."""
+def sq(sq_dir: str, trace_dir: str, skip: int = 2, count: int = 5):
+    """Per kernel: SQ counters of one dispatch and, with the kernel trace's
+    average over the timed launches (after `skip` warm-ups, `count` of
+    them), the achieved VALU lane-operation rate."""
     per = {c: counter_per_kernel(sq_dir, c) for c in SQ_COUNTERS}
-    dur = {}
-    for name, calls, avg_us, tot, pct in kernel_stats(trace_dir):
-        for short, frag in KERNELS.items():
-            if frag in name:
-                dur[short] = avg_us
+    dur = {k: us for k, (n, us) in timed_average(trace_dir, skip, count).items()}
     out = {}
     for k in per["SQ_INSTS_VALU"]:
         e = {c: per[c].get(k) for c in SQ_COUNTERS}
@@ -210,7 +210,7 @@ def main():
                     "(SQ_WAVE_CYCLES). Waiting: at an s_waitcnt; LDS issue: waiting to issue an LDS "
                     "instruction; scalar: issuing scalar ALU; misc: branches and other sequencer "
                     "instructions. Two counter passes (at most 8 SQ counters each) over the same "
-                    "one-step run.\n\n" % source_hash())
+                    "one-step run; the first dispatch of each kernel (the step's).\n\n" % source_hash())
             f.write("Commands (repository root):\n\n```\n%s\n```\n\n" % a.command.replace(";", "\n"))
             f.write("| kernel | waves' cycles | waiting (s_waitcnt) | waiting to issue LDS | issuing any | "
                     "issuing scalar ALU | branches/misc | VALU insts | LDS data FIFO full |\n"
@@ -240,7 +240,7 @@ def main():
         with open(a.md, "w") as f:
             f.write("# SQ counters per launch, %s workload (rocprofv3)\n\n" % a.config)
             f.write("Kernel sources: hash `%s`. VALU peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = %.2f T "
-                    "lane-ops/s (int32 / non-packed fp32). Durations: the kernel-trace run.\n\n"
+                    "lane-ops/s (int32 / non-packed fp32). Counters: the first dispatch of each kernel (the one timed step). Durations: the kernel-trace run's timed launches (after 2 warm-up steps, the 5 timed steps).\n\n"
                     % (source_hash(), VALU_PEAK_OPS / 1e12))
             f.write("Commands (repository root):\n\n```\n%s\n```\n\n" % a.command.replace(";", "\n"))
             f.write("| kernel | avg us | waves | VALU insts | SALU insts | LDS insts | VALU lane-ops/s | of VALU "
