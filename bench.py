@@ -585,8 +585,10 @@ def run_level_mix(args, cfg, cd, x, shp, stream):
                 q = np.nan_to_num(q).astype(np.int32)
                 ref = torch.from_numpy(q.astype(np.float32) * st).to(x.dtype).view(torch.int16).numpy().view(np.uint16)
             assert np.array_equal(got[rows], ref), (l, kv, h, c)
+    # the method's bytes: fp16 out, records in, each level's tables' format
+    # section (512 B per table), as in the round-trip line
     n_tables = sum(2 * lv.n_groups * cfg.kv_heads * cfg.head_dim for lv in lvs)
-    dec_bytes = fp16_bytes + comp + n_tables * 2048
+    dec_bytes = fp16_bytes + comp + n_tables * 512
     gbps = dec_bytes / (kern / 1e3) / 1e9
     res = {
         "metric": METRIC,
