@@ -21,6 +21,13 @@ CASES = [
     # 64 layers in one group (two rounds), 60 + 40 layers (rounds of 48 + 12)
     ("64-layers-one-group", 64, 1, 64, 40, 16, [0] * 64, [0.8], 6),
     ("100-layers-two-groups", 100, 1, 64, 33, 33, [0] * 60 + [1] * 40, [0.5, 1.5], 7),
+    # every chunk one token (records hold only heads, no symbols)
+    ("one-token-chunks", 2, 2, 64, 9, 1, [0, 1], [0.5, 1.0], 8),
+    # the largest layer count the library takes, in one group (22 decode
+    # rounds of 48 items per record)
+    ("1024-layers", 1024, 1, 64, 6, 4, [0] * 1024, [0.8], 9),
+    # head_dim 256: four 64-channel slices per head
+    ("d256", 2, 2, 256, 70, 32, [0, 1], [0.3, 1.2], 10),
 ]
 
 
