@@ -678,22 +678,39 @@ __global__ void __launch_bounds__(kNormThreads) k_norm(NormArgs a) {
 constexpr int kEncThreads = kWaves * 64;
 constexpr int kEncBatch = 16;
 
-// On the lanes of m: store the low 16 bits of x at byte voff + soff of sr,
+// The encoder's scratch slot is a structured buffer of 2-byte records (one
+// word each, cap of them), so a store names its word by index and the
+// address unit does the doubling: word soff/2 + idx. Stores only, in inline
+// assembly (the compiler has no structured 16-bit store); no memory clobber:
+// nothing in the kernel reads the scratch it writes, and a clobber would keep
+// the next token's table read from moving above the store.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_slot_rsrc(const uint16_t* base, uint32_t words) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)2, (int)words, 0x00020000);
+}
+
+// word idx (per lane) after the first soff / 2 words of the slot <- v
+__device__ __forceinline__ void slot_store(uint32_t v, uint32_t idx, __amdgpu_buffer_rsrc_t sw, uint32_t soff) {
+  asm volatile(
+      "s_nop 4\n\t"  // VALU-written SGPR operands of the store: see stream_load_async
+      "buffer_store_short %0, %1, %2, %3 idxen"
+      :
+      : "v"(v), "v"(idx), "s"(sw), "s"(soff));
+}
+
+// On the lanes of m: store the low 16 bits of x as word idx after soff / 2,
 // then x >>= 16. One masked region with a single VALU shift; the compiler's
-// version computes the shift into a temporary and copies it back. No memory
-// clobber: nothing in the kernel reads the scratch it writes, and a clobber
-// would keep the next token's table read from moving above the store.
-__device__ __forceinline__ void renorm_out(uint32_t& x, uint64_t m, __amdgpu_buffer_rsrc_t sr,
-                                           uint32_t voff, uint32_t soff) {
+// version computes the shift into a temporary and copies it back.
+__device__ __forceinline__ void renorm_out(uint32_t& x, uint64_t m, __amdgpu_buffer_rsrc_t sw,
+                                           uint32_t idx, uint32_t soff) {
   uint64_t saved;
   asm volatile(
       "s_nop 4\n\t"  // VALU-written SGPR operands of the store: see stream_load_async
       "s_and_saveexec_b64 %1, %2\n\t"
-      "buffer_store_short %0, %3, %4, %5 offen\n\t"
+      "buffer_store_short %0, %3, %4, %5 idxen\n\t"
       "v_lshrrev_b32 %0, 16, %0\n\t"
       "s_mov_b64 exec, %1"
       : "+v"(x), "=&s"(saved)
-      : "s"(m), "v"(voff), "s"(sr), "s"(soff)
+      : "s"(m), "v"(idx), "s"(sw), "s"(soff)
       : "scc");
 }
 
@@ -754,13 +771,13 @@ __device__ __forceinline__ void enc_s3(const EncTok& k, uint32_t& x, uint32_t& P
                                        int32_t* status, int lane) {
   if (k.me) {
     P -= (uint32_t)__popcll(k.me);
-    if (k.esc) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)k.d16, sr, 2u * mbcnt_base(k.me, 0), 2u * P, 0);
+    if (k.esc) slot_store(k.d16, mbcnt_base(k.me, 0), sr, 2u * P);
     if (__builtin_expect(__ballot(k.esc && k.f == 0) != 0, 0) && lane == 0) set_status(status, CG_ERR_TABLE);
   }
   // renormalise when x >= f * 2^20, i.e. floor(x / 2^20) >= f (never for f = 4096)
   const uint64_t mr = __ballot((x >> 20) >= k.f);
   P -= (uint32_t)__popcll(mr);
-  renorm_out(x, mr, sr, 2u * mbcnt_base(mr, 0), 2u * P);
+  renorm_out(x, mr, sr, mbcnt_base(mr, 0), 2u * P);
   // x <- floor(x/f)*4096 + x mod f + b = x + floor(x/f)*(4096-f) + b; the
   // quotient is < 2^20 and 4096 - f < 2^12, so a 24-bit multiply is exact.
   // (f = 0 only for a symbol missing from the table: the group is then
@@ -874,11 +891,11 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
     enc_s3(a, x, P, sr, status, lane);
   }
   P -= 64;
-  __builtin_amdgcn_raw_buffer_store_b16((uint16_t)qhi, sr, lane2, 2u * P, 0);
+  slot_store((uint32_t)qhi, lane, sr, 2u * P);
   P -= 64;
-  __builtin_amdgcn_raw_buffer_store_b16((uint16_t)x, sr, lane2, 2u * P, 0);
+  slot_store(x, lane, sr, 2u * P);
   P -= 64;
-  __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(x >> 16), sr, lane2, 2u * P, 0);
+  slot_store(x >> 16, lane, sr, 2u * P);
   words = cap - P;
   start = P;
 }
@@ -979,7 +996,7 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
     const int l = layer_of_group(a.blob, G, s.L, g, it % lg_count, lane);
     const int64_t gi = (((int64_t)l * 2 + kv) * s.H + h) * s.S + j;
     const int64_t slot = cl * gpc + gi;
-    const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.scratch + (size_t)slot * a.cap_words, 2u * cap);
+    const __amdgpu_buffer_rsrc_t sr = make_slot_rsrc(a.scratch + (size_t)slot * a.cap_words, cap);
     const uint16_t* xb = a.x + ((((size_t)l * 2 + kv) * s.H + h) * (size_t)s.T + t0) * s.D + 64 * j;
     const uint32_t row_bytes = 2u * (uint32_t)s.D;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(xb, (uint32_t)n * row_bytes);
