@@ -667,7 +667,7 @@ __global__ void __launch_bounds__(kNormThreads) k_norm(NormArgs a) {
 // ---------------------------------------------------------------------------
 // encode: one workgroup per (chunk, layer group, K|V, head, slice); its 16
 // wavefronts take the layers of the group. The set's encoder table (lane-
-// minor, 64 KB) and RU(1/f) for f = 1..4096 (32 KB) sit in LDS.
+// minor, 64 KB) and per f = 0..4096 RU(1/f), 4096 - f and f * 2^20 - 1 (64 KB) sit in LDS.
 // Exact quotient: floor(x/f) = trunc(fl64(x) * RU(1/f)) for x < 2^32, f <= 2^12
 // (the product stays below q+1 by more than the fp64 spacing there).
 // The group is coded backward (token n-1 first) and its words are written
@@ -725,8 +725,17 @@ struct EncTok {
   uint32_t d16;  // low 16 bits: the wrapped delta, the escape payload
   bool esc;      // this lane codes an escape (wide delta, or robust tables)
   uint64_t me;   // lanes of the wavefront that need one
-  uint32_t f;
-  double r;      // RU(1/f) (S2 read)
+  double r;      // RU(1/f)          } the frequency's constants (S2 read,
+  uint32_t g;    // 4096 - f         } one 16-byte LDS entry)
+  uint32_t t;    // f * 2^20 - 1: renormalise when x > t
+};
+
+// Per-frequency constants of the encoder, one 16-byte LDS entry per f.
+// f = 0 (a symbol missing from plain tables, reported as CG_ERR_TABLE) gets
+// r = 0, g = 4096 and t = 2^32 - 1, which keep the state finite.
+struct alignas(16) FreqK {
+  double r;
+  uint32_t g, t;
 };
 
 // q_t - q_{t-1} wrapped to 16 bits and sign-extended, in one instruction
@@ -755,11 +764,13 @@ __device__ __forceinline__ void enc_s1(EncTok& k, uint16_t xprev, int32_t& qhi, 
 
 // the escape decision comes from the entry: symbol 255 (a wide delta) and,
 // with robust tables, every symbol of frequency 0 carry the flag
-__device__ __forceinline__ void enc_s2(EncTok& k, const double* rcp_tab) {
+__device__ __forceinline__ void enc_s2(EncTok& k, const FreqK* fk) {
   k.esc = (int32_t)k.e < 0;
   k.me = __ballot(k.esc);
-  k.f = k.e & 0xFFFFu;
-  k.r = rcp_tab[k.f];
+  const uint4 w = reinterpret_cast<const uint4*>(fk)[k.e & 0xFFFFu];
+  k.r = __hiloint2double((int)w.y, (int)w.x);
+  k.g = w.z;
+  k.t = w.w;
 }
 
 // Every entry of frequency 0 carries the escape flag (see k_norm), so an
@@ -772,18 +783,17 @@ __device__ __forceinline__ void enc_s3(const EncTok& k, uint32_t& x, uint32_t& P
   if (k.me) {
     P -= (uint32_t)__popcll(k.me);
     if (k.esc) slot_store(k.d16, mbcnt_base(k.me, 0), sr, 2u * P);
-    if (__builtin_expect(__ballot(k.esc && k.f == 0) != 0, 0) && lane == 0) set_status(status, CG_ERR_TABLE);
+    if (__builtin_expect(__ballot(k.esc && (k.e & 0xFFFFu) == 0) != 0, 0) && lane == 0)
+      set_status(status, CG_ERR_TABLE);
   }
-  // renormalise when x >= f * 2^20, i.e. floor(x / 2^20) >= f (never for f = 4096)
-  const uint64_t mr = __ballot((x >> 20) >= k.f);
+  // renormalise when x >= f * 2^20 (never for f = 4096: x < 2^32)
+  const uint64_t mr = __ballot(x > k.t);
   P -= (uint32_t)__popcll(mr);
   renorm_out(x, mr, sr, mbcnt_base(mr, 0), 2u * P);
   // x <- floor(x/f)*4096 + x mod f + b = x + floor(x/f)*(4096-f) + b; the
   // quotient is < 2^20 and 4096 - f < 2^12, so a 24-bit multiply is exact.
-  // (f = 0 only for a symbol missing from the table: the group is then
-  // invalid and CG_ERR_TABLE is reported; rcp_tab[0] = 0 keeps it finite)
   const uint32_t qd = (uint32_t)((double)x * k.r);
-  x = __umul24(qd, kM - k.f) + x + ((k.e >> 16) & 0x7FFFu);
+  x = __umul24(qd, k.g) + x + ((k.e >> 16) & 0x7FFFu);
 }
 
 // Encodes tokens n-1 .. 1 of a group (backward), then the head. xr covers the
@@ -792,7 +802,7 @@ __device__ __forceinline__ void enc_s3(const EncTok& k, uint32_t& x, uint32_t& P
 template <int QM, bool BF>
 __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, uint32_t row_bytes,
                                              float step, float rcp, const uint32_t* ftab,
-                                             const double* rcp_tab, __amdgpu_buffer_rsrc_t sr,
+                                             const FreqK* fk, __amdgpu_buffer_rsrc_t sr,
                                              uint32_t cap, int lane, uint32_t& words,
                                              uint32_t& start, int32_t* status, int* left, int wave,
                                              int left_after) {
@@ -808,7 +818,7 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
     // S2, token n-2 through S1.
     EncTok a, b, c;
     enc_s1<QM, BF>(a, row(n - 2), qhi, step, rcp, row0);
-    enc_s2(a, rcp_tab);
+    enc_s2(a, fk);
     enc_s1<QM, BF>(b, row(n - 3), qhi, step, rcp, row0);
     // tokens i, i-1, ... enter S1 with x of rows i-1, i-2, ...; the rows of
     // the next batch are loaded while the current one is encoded. Offsets
@@ -843,7 +853,7 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
     __builtin_amdgcn_s_waitcnt(0x0F70);  // as in hist_range
     auto advance = [&](uint16_t xprev) {
       enc_s1<QM, BF>(c, xprev, qhi, step, rcp, row0);
-      enc_s2(b, rcp_tab);
+      enc_s2(b, fk);
       enc_s3(a, x, P, sr, status, lane);
       a = b;
       b = c;
@@ -881,13 +891,13 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
     for (int k = 0; k < kEncBatch; ++k)  // the last i < 16 tokens
       if (k < i) advance((uint16_t)xa[k]);
     // epilogue: the last two tokens leave the pipeline
-    enc_s2(b, rcp_tab);
+    enc_s2(b, fk);
     enc_s3(a, x, P, sr, status, lane);
     enc_s3(b, x, P, sr, status, lane);
   } else if (n == 2) {
     EncTok a;
     enc_s1<QM, BF>(a, row(0), qhi, step, rcp, row0);
-    enc_s2(a, rcp_tab);
+    enc_s2(a, fk);
     enc_s3(a, x, P, sr, status, lane);
   }
   P -= 64;
@@ -928,15 +938,16 @@ __device__ __forceinline__ int layers_in_group(const uint8_t* blob, int G, int L
 }
 
 // LDS of the encoder, laid out by hand so both tables sit at small fixed
-// offsets: the reciprocals first (address f * 8), then the symbol table.
-constexpr int kEncRcpBytes = 8 * (kM + 1);
+// offsets: the per-frequency constants first (address f * 16), then the
+// symbol table.
+constexpr int kEncRcpBytes = 16 * (kM + 1);
 constexpr int kEncFtabOff = (kEncRcpBytes + 255) / 256 * 256;
 
 template <bool BF>
 __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
   __shared__ __align__(16) uint8_t enc_lds[kEncFtabOff + 4 * kEncDwords * 64];
   __shared__ int left[kWaves];
-  double* rcp_tab = reinterpret_cast<double*>(enc_lds);
+  FreqK* fk = reinterpret_cast<FreqK*>(enc_lds);
   uint32_t* ftab = reinterpret_cast<uint32_t*>(enc_lds + kEncFtabOff);
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const Shape s = a.s;
@@ -970,9 +981,9 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
   for (int f = tid + 1; f <= (int)kM; f += kEncThreads) {
     double r = 1.0 / (double)f;
     if (__builtin_fma(r, (double)f, -1.0) < 0.0) r = __longlong_as_double(__double_as_longlong(r) + 1);
-    rcp_tab[f] = r;
+    fk[f] = FreqK{r, kM - (uint32_t)f, (uint32_t)(((uint64_t)f << 20) - 1)};
   }
-  if (tid == 0) rcp_tab[0] = 0.0;
+  if (tid == 0) fk[0] = FreqK{0.0, kM, 0xFFFFFFFFu};
   if (tid < kWaves) left[tid] = 0x7FFFFFFF;
   __syncthreads();
 
@@ -1002,7 +1013,7 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(xb, (uint32_t)n * row_bytes);
     uint32_t words, start;
 #define CG_ENC(QM) \
-  encode_group<QM, BF>(xr, (int)n, row_bytes, step, rcp, ftab, rcp_tab, sr, cap, lane, words, start, a.status, \
+  encode_group<QM, BF>(xr, (int)n, row_bytes, step, rcp, ftab, fk, sr, cap, lane, words, start, a.status, \
                left, wave, my_left)
     if (qm == kQuotMul) CG_ENC(kQuotMul);
     else if (qm == kQuotFma) CG_ENC(kQuotFma);
