@@ -103,32 +103,46 @@ __device__ __forceinline__ float cvt_f32_sext16(int32_t v) {
 // q = clamp(rint_even(fl32(x / step)), -32768, 32767), NaN -> 0.
 // Three ways to the quotient, QM:
 //   kQuotDiv   the IEEE binary32 divide;
-//   kQuotFma   v1 = x*r, e = x - v1*step (exact by FMA), v = v1 + e*r with
-//              r = RN(1/step);
-//   kQuotMul   v = x*r.
+//   kQuotTwo   v = fma(x, r_hi, x * r_lo): a two-term reciprocal, r_hi = 1/step
+//              rounded down, r_lo = RN(1/step - r_hi) >= 0, so x * r_lo has
+//              the sign of x (+-Inf and overflow stay saturating, NaN NaN);
+//              its error is ~2^-48 relative, far inside the quotient's
+//              rounding except where the divide rounds onto a tie;
+//   kQuotMul   v = x * RN(1/step).
 // The two cheap ones are used only for steps where k_qcheck proved that they
 // give the same q as the divide for every input of the element type.
 // Branch-free; sat / nan_ count saturated and NaN inputs.
-constexpr int kQuotDiv = 0, kQuotFma = 1, kQuotMul = 2;
+constexpr int kQuotDiv = 0, kQuotTwo = 1, kQuotMul = 2;
+
+// The constants of one step, computed once per workgroup.
+struct Quot {
+  float step;
+  float rcp;  // RN(1/step)
+  float rhi;  // 1/step rounded down
+  float rlo;  // RN(1/step - rhi)
+};
+
+__device__ __forceinline__ Quot make_quot(float step) {
+  Quot q;
+  q.step = step;
+  q.rcp = 1.0f / step;
+  // rcp * step - 1 with one rounding keeps the sign of the exact value
+  q.rhi = __builtin_fmaf(q.rcp, step, -1.0f) > 0.0f ? __uint_as_float(__float_as_uint(q.rcp) - 1u) : q.rcp;
+  q.rlo = (float)(1.0 / (double)step - (double)q.rhi);
+  return q;
+}
 
 template <int QM, bool BF>
-__device__ __forceinline__ int32_t quantize(uint16_t xh, float step, float rcp, uint32_t& sat,
-                                            uint32_t& nan_) {
+__device__ __forceinline__ int32_t quantize(uint16_t xh, const Quot& qc, uint32_t& sat, uint32_t& nan_) {
   constexpr bool FAST = QM != kQuotDiv;
   const float x = elem_to_f32<BF>(xh);
   float v;
   if (QM == kQuotMul) {
-    v = x * rcp;  // NaN stays NaN, Inf and overflow saturate below
-  } else if (QM == kQuotFma) {
-    // x*r clamped to +-65536 first, so the correction is finite unless x
-    // is NaN (then NaN -> 0, as the quotient): a finite x beyond the clamp
-    // (bfloat16 reaches 3.4e38) or an infinite one lands beyond +-32767.5
-    // and saturates as the quotient does; inside it nothing changes
-    const float v1 = __builtin_amdgcn_fmed3f(x * rcp, -65536.0f, 65536.0f);
-    const float e = __builtin_fmaf(-v1, step, x);
-    v = __builtin_fmaf(e, rcp, v1);
+    v = x * qc.rcp;  // NaN stays NaN, Inf and overflow saturate below
+  } else if (QM == kQuotTwo) {
+    v = __builtin_fmaf(x, qc.rhi, x * qc.rlo);
   } else {
-    v = x / step;
+    v = x / qc.step;
   }
   const bool is_nan = v != v;
   const float r = __builtin_rintf(v);
@@ -268,11 +282,11 @@ __device__ __forceinline__ bool blob_ok(const uint8_t* b, const Shape& s, int G)
          (int)uni(bh->H) == s.H && (int)uni(bh->D) == s.D && (int)uni(bh->G) == G &&
          (int)uni(bh->dtype) == s.dt && (uni(bh->flags) & ~kTablesRobust) == 0;
 }
-// Quotient mode of layer group g: bit 0 of the flag = kQuotFma proven exact,
+// Quotient mode of layer group g: bit 0 of the flag = kQuotTwo proven exact,
 // bit 1 = kQuotMul proven exact (k_qcheck clears what fails).
 __device__ __forceinline__ int qmode(const uint8_t* b, int L, int H, int D, int G, int g) {
   const uint32_t f = uni(reinterpret_cast<const uint32_t*>(b + tb_qflag_offset(L, H, D, G))[g]);
-  return (f & 2u) ? kQuotMul : (f & 1u) ? kQuotFma : kQuotDiv;
+  return (f & 2u) ? kQuotMul : (f & 1u) ? kQuotTwo : kQuotDiv;
 }
 
 // ---------------------------------------------------------------------------
@@ -359,12 +373,11 @@ template <bool BF>
 __global__ void k_qcheck(QCheckArgs a) {
   const int g = blockIdx.y;
   const uint32_t xh = blockIdx.x * blockDim.x + threadIdx.x;  // 0 .. 65535
-  const float step = blob_step(a.blob, g);
-  const float rcp = 1.0f / step;
+  const Quot qc = make_quot(blob_step(a.blob, g));
   uint32_t s0 = 0, n0 = 0;
-  const int32_t qi = quantize<kQuotDiv, BF>((uint16_t)xh, step, rcp, s0, n0);
-  const int32_t qf = quantize<kQuotFma, BF>((uint16_t)xh, step, rcp, s0, n0);
-  const int32_t qm = quantize<kQuotMul, BF>((uint16_t)xh, step, rcp, s0, n0);
+  const int32_t qi = quantize<kQuotDiv, BF>((uint16_t)xh, qc, s0, n0);
+  const int32_t qf = quantize<kQuotTwo, BF>((uint16_t)xh, qc, s0, n0);
+  const int32_t qm = quantize<kQuotMul, BF>((uint16_t)xh, qc, s0, n0);
   if (qf != qi) atomicAnd(&a.qflags[g], ~1u);
   if (qm != qi) atomicAnd(&a.qflags[g], ~2u);
 }
@@ -386,7 +399,7 @@ constexpr int kHistBatch = 16;
 // is in bounds by construction. STATS adds the saturated / NaN counts.
 template <int QM, bool STATS, bool BF>
 __device__ __forceinline__ void hist_range(__amdgpu_buffer_rsrc_t xr, uint32_t row_bytes, int t_begin,
-                                           int t_end, int C, float step, float rcp, uint32_t* hist,
+                                           int t_end, int C, const Quot qc, uint32_t* hist,
                                            int* left, int wave, int lane, uint32_t& sat,
                                            uint32_t& nan_) {
   const uint32_t lane2 = 2u * lane, lane4 = 4u * lane;
@@ -397,11 +410,11 @@ __device__ __forceinline__ void hist_range(__amdgpu_buffer_rsrc_t xr, uint32_t r
     uint32_t d0 = 0, d1 = 0;
     prev = quantize<QM, BF>(
         (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, (uint32_t)(t_begin - 1) * row_bytes, 0),
-        step, rcp, d0, d1);
+        qc, d0, d1);
   }
   auto one = [&](uint16_t xh) {
     uint32_t s0 = 0, n0 = 0;
-    const int32_t q = quantize<QM, BF>(xh, step, rcp, s0, n0);
+    const int32_t q = quantize<QM, BF>(xh, qc, s0, n0);
     if (STATS) {
       sat += s0;
       nan_ += n0;
@@ -477,8 +490,7 @@ __global__ void __launch_bounds__(kHistThreads) k_hist(HistArgs a) {
   const int l = (int)(bid / 2);
   const int G = a.G;
   const int g = layer_group(a.blob, G, l);
-  const float step = blob_step(a.blob, g);
-  const float rcp = 1.0f / step;
+  const Quot qc = make_quot(blob_step(a.blob, g));
   const int qm = qmode(a.blob, s.L, s.H, s.D, G, g);
   __syncthreads();
 
@@ -489,14 +501,14 @@ __global__ void __launch_bounds__(kHistThreads) k_hist(HistArgs a) {
   uint32_t sat = 0, nan_ = 0;
   if (t_begin < t_end) {
 #define CG_HIST(QM, ST) \
-  hist_range<QM, ST, BF>(xr, row_bytes, t_begin, t_end, s.C, step, rcp, hist, left, wave, lane, sat, nan_)
+  hist_range<QM, ST, BF>(xr, row_bytes, t_begin, t_end, s.C, qc, hist, left, wave, lane, sat, nan_)
     if (a.stats) {
       if (qm == kQuotMul) CG_HIST(kQuotMul, true);
-      else if (qm == kQuotFma) CG_HIST(kQuotFma, true);
+      else if (qm == kQuotTwo) CG_HIST(kQuotTwo, true);
       else CG_HIST(kQuotDiv, true);
     } else {
       if (qm == kQuotMul) CG_HIST(kQuotMul, false);
-      else if (qm == kQuotFma) CG_HIST(kQuotFma, false);
+      else if (qm == kQuotTwo) CG_HIST(kQuotTwo, false);
       else CG_HIST(kQuotDiv, false);
     }
 #undef CG_HIST
@@ -751,10 +763,10 @@ __device__ __forceinline__ int32_t sub_wrap16(int32_t a, int32_t b) {
 // row0: the lane's column of the encoder table at row 128 (delta 0); the
 // entry of delta d is row0[64 * clamp(d, -128, 128)]
 template <int QM, bool BF>
-__device__ __forceinline__ void enc_s1(EncTok& k, uint16_t xprev, int32_t& qhi, float step, float rcp,
+__device__ __forceinline__ void enc_s1(EncTok& k, uint16_t xprev, int32_t& qhi, const Quot& qc,
                                        const uint32_t* row0) {
   uint32_t d0 = 0, d1 = 0;
-  const int32_t qlo = quantize<QM, BF>(xprev, step, rcp, d0, d1);
+  const int32_t qlo = quantize<QM, BF>(xprev, qc, d0, d1);
   const int32_t d = sub_wrap16(qhi, qlo);
   k.d16 = (uint32_t)d;
   const int32_t m = d < -128 ? -128 : (d > 128 ? 128 : d);
@@ -801,7 +813,7 @@ __device__ __forceinline__ void enc_s3(const EncTok& k, uint32_t& x, uint32_t& P
 // cap words; every access is in bounds by construction.
 template <int QM, bool BF>
 __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, uint32_t row_bytes,
-                                             float step, float rcp, const uint32_t* ftab,
+                                             const Quot qc, const uint32_t* ftab,
                                              const FreqK* fk, __amdgpu_buffer_rsrc_t sr,
                                              uint32_t cap, int lane, uint32_t& words,
                                              uint32_t& start, int32_t* status, int* left, int wave,
@@ -812,14 +824,14 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
   uint32_t x = kL;
   auto row = [&](int r) { return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, (uint32_t)r * row_bytes, 0); };
   uint32_t d0 = 0, d1 = 0;
-  int32_t qhi = quantize<QM, BF>(row(n - 1), step, rcp, d0, d1);
+  int32_t qhi = quantize<QM, BF>(row(n - 1), qc, d0, d1);
   if (n >= 3) {
     // a: token in S3, b: in S2, c: in S1. Prologue: token n-1 through S1 and
     // S2, token n-2 through S1.
     EncTok a, b, c;
-    enc_s1<QM, BF>(a, row(n - 2), qhi, step, rcp, row0);
+    enc_s1<QM, BF>(a, row(n - 2), qhi, qc, row0);
     enc_s2(a, fk);
-    enc_s1<QM, BF>(b, row(n - 3), qhi, step, rcp, row0);
+    enc_s1<QM, BF>(b, row(n - 3), qhi, qc, row0);
     // tokens i, i-1, ... enter S1 with x of rows i-1, i-2, ...; the rows of
     // the next batch are loaded while the current one is encoded. Offsets
     // stay scalar: a batch of 16 rows all >= 0 needs no clamp; the last one
@@ -852,7 +864,7 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
     load_rows_clamped(xb, i - kEncBatch);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // as in hist_range
     auto advance = [&](uint16_t xprev) {
-      enc_s1<QM, BF>(c, xprev, qhi, step, rcp, row0);
+      enc_s1<QM, BF>(c, xprev, qhi, qc, row0);
       enc_s2(b, fk);
       enc_s3(a, x, P, sr, status, lane);
       a = b;
@@ -896,7 +908,7 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
     enc_s3(b, x, P, sr, status, lane);
   } else if (n == 2) {
     EncTok a;
-    enc_s1<QM, BF>(a, row(0), qhi, step, rcp, row0);
+    enc_s1<QM, BF>(a, row(0), qhi, qc, row0);
     enc_s2(a, fk);
     enc_s3(a, x, P, sr, status, lane);
   }
@@ -987,8 +999,7 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
   if (tid < kWaves) left[tid] = 0x7FFFFFFF;
   __syncthreads();
 
-  const float step = blob_step(a.blob, g);
-  const float rcp = 1.0f / step;
+  const Quot qc = make_quot(blob_step(a.blob, g));
   const int qm = qmode(a.blob, s.L, s.H, s.D, G, g);
   const int64_t gpc = groups_per_chunk(s.L, s.H, s.D);
   const uint32_t cap = (uint32_t)a.cap_words;
@@ -1013,10 +1024,10 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(xb, (uint32_t)n * row_bytes);
     uint32_t words, start;
 #define CG_ENC(QM) \
-  encode_group<QM, BF>(xr, (int)n, row_bytes, step, rcp, ftab, fk, sr, cap, lane, words, start, a.status, \
+  encode_group<QM, BF>(xr, (int)n, row_bytes, qc, ftab, fk, sr, cap, lane, words, start, a.status, \
                left, wave, my_left)
     if (qm == kQuotMul) CG_ENC(kQuotMul);
-    else if (qm == kQuotFma) CG_ENC(kQuotFma);
+    else if (qm == kQuotTwo) CG_ENC(kQuotTwo);
     else CG_ENC(kQuotDiv);
 #undef CG_ENC
     if (lane == 0) {

@@ -29,7 +29,7 @@ CASES = [
      lambda: synth.random_kv_bf16(2, 1, 64, 300, 32, scale=1e6), None),
     ("bf16-every-pattern", 1, 1, 64, 1024, 256, [0], [0.37], BF16, 0, all_bf16_patterns, None),
     # every bf16 input at each of the nine preset steps ("CacheGen实战" 3.1),
-    # whose quotients take the multiply or one-FMA paths
+    # whose quotients take the multiply or two-term-reciprocal paths
     ("bf16-every-pattern-presets", 9, 1, 64, 1024, 256, list(range(9)),
      [0.3, 0.8, 1.2, 0.5, 1.0, 1.5, 0.8, 1.5, 2.0], BF16, 0,
      lambda: np.concatenate([all_bf16_patterns()] * 9), None),

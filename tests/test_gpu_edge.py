@@ -2,7 +2,7 @@
 every fp16 bit pattern (NaN, +-Inf, subnormals, saturation) at a step that
 takes the IEEE divide and at each of the nine preset steps ("CacheGen实战"
 section 3.1: 0.3/0.8/1.2, 0.5/1.0/1.5, 0.8/1.5/2.0), whose quotients take
-the multiply or one-FMA paths, a tensor where every delta needs an escape
+the multiply or two-term-reciprocal paths, a tensor where every delta needs an escape
 (the worst-case stream size), one layer group per layer, and the largest
 group count (255)."""
 import numpy as np
@@ -69,7 +69,7 @@ def test_tables_and_stats(pair):
         assert int(o["stats"][2]) == 9 * 2 * 2046
         # the quotient paths the tables chose (library lookup section, right
         # after the format section: u32 per layer group, bit 1 = multiply,
-        # bit 0 = one-FMA correction, proven exact over every input): both
+        # bit 0 = two-term reciprocal, proven exact over every input): both
         # fast paths are exercised, so the byte checks cover them
         qoff = -(-fb // 256) * 256
         qf = U.u8(g["tables"])[qoff:qoff + 4 * 9].view(np.uint32)
