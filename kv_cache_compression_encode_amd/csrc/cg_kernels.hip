@@ -13,8 +13,8 @@
 // Kernels
 //   k_fill_u32     fill (no hipMemset, so calls stay capturable)
 //   k_blob_init    tables-blob header, steps, layer groups
-//   k_qcheck       per layer group: is x*(1/step), or failing that its one-FMA
-//                  correction, exact for all 65536 inputs of the element type?
+//   k_qcheck       per layer group: is x*(1/step), or failing that a two-term
+//                  reciprocal, exact for all 65536 inputs of the element type?
 //                  (else the IEEE divide is used)
 //   k_hist         quantize + delta + symbol, LDS-privatised 64 x 256 counts
 //   k_norm         one wavefront per table: 12-bit normalisation, cumulative
