@@ -137,10 +137,14 @@ __device__ __forceinline__ int32_t quantize(uint16_t xh, const Quot& qc, uint32_
   constexpr bool FAST = QM != kQuotDiv;
   const float x = elem_to_f32<BF>(xh);
   float v;
+  // (the products written as fma with a zero addend round as the plain
+  // products do, apart from the sign of a zero quotient, which q does not
+  // see; for fp16 inputs the backend then folds the conversion of x into
+  // mixed-precision fma instructions)
   if (QM == kQuotMul) {
-    v = x * qc.rcp;  // NaN stays NaN, Inf and overflow saturate below
+    v = __builtin_fmaf(x, qc.rcp, 0.0f);  // NaN stays NaN, Inf and overflow saturate below
   } else if (QM == kQuotTwo) {
-    v = __builtin_fmaf(x, qc.rhi, x * qc.rlo);
+    v = __builtin_fmaf(x, qc.rhi, __builtin_fmaf(x, qc.rlo, 0.0f));
   } else {
     v = x / qc.step;
   }
