@@ -635,22 +635,27 @@ __global__ void __launch_bounds__(kNormThreads) k_norm(NormArgs a) {
   fv.x = f[0] | (f[1] << 16);
   fv.y = f[2] | (f[3] << 16);
   reinterpret_cast<uint2*>(fsec)[lane] = fv;
-  // encoder set: f | b << 16 | escape << 31 per symbol. The escape
-  // symbol's entry carries the flag; with robust tables a symbol of
-  // frequency 0 gets the escape's entry, so the encoder escapes it.
-  // Without, such a symbol gets the flag with f = 0: the encoder's escape
-  // branch (the only place it looks) reports an escaping lane whose entry
-  // has f = 0, which also covers an escape symbol of frequency 0.
-  // Rows are indexed by delta + 128 (symbol + 1); the escape's entry fills
-  // rows 0 and 256, which the clamped deltas beyond +-127 reach.
+  // encoder set: (16 f - 1) mod 2^16 | b << 16 per symbol. The low half
+  // gives the encoder both its renormalisation test (x >> 16 above it) and
+  // the address of f's reciprocal (8 f, from half of it); the high half is
+  // the symbol's start. The escape symbol (255) comes last in cumulative
+  // order, so every other coded symbol's entry is below the escape's: the
+  // encoder escapes a lane whose entry is at or above it. With robust
+  // tables a symbol of frequency 0 gets the escape's entry, so the encoder
+  // escapes it; without, it gets kEncInvalid, which is at or above any
+  // escape entry, as is the escape of plain tables that saw none; the
+  // encoder's escape branch reports kEncInvalid as CG_ERR_TABLE. Rows are
+  // indexed by delta + 128 (symbol + 1); the escape's entry fills rows 0
+  // and 256, which the clamped deltas beyond +-127 reach.
   uint32_t* enc = reinterpret_cast<uint32_t*>(a.blob + a.enc_off) + set * (kEncDwords * 64) + kk;
-  const uint32_t esc_entry = __shfl(f[3] | (b[3] << 16), 63) | 0x80000000u;
+  const uint32_t f_esc = __shfl(f[3], 63), b_esc = __shfl(b[3], 63);
+  const uint32_t esc_entry = f_esc == 0 ? kEncInvalid : (((16u * f_esc - 1u) & 0xFFFFu) | (b_esc << 16));
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int sym = 4 * lane + k;
-    uint32_t e = f[k] | (b[k] << 16);
+    uint32_t e = ((16u * f[k] - 1u) & 0xFFFFu) | (b[k] << 16);
     if (sym == 255) e = esc_entry;
-    else if (f[k] == 0) e = a.robust ? esc_entry : (esc_entry & 0xFFFF0000u);
+    else if (f[k] == 0) e = a.robust ? esc_entry : kEncInvalid;
     if (sym < 255) {
       enc[(sym + 1) * 64] = e;
     } else {
@@ -683,7 +688,8 @@ __global__ void __launch_bounds__(kNormThreads) k_norm(NormArgs a) {
 // ---------------------------------------------------------------------------
 // encode: one workgroup per (chunk, layer group, K|V, head, slice); its 16
 // wavefronts take the layers of the group. The set's encoder table (lane-
-// minor, 64 KB) and per f = 0..4096 RU(1/f), 4096 - f and f * 2^20 - 1 (64 KB) sit in LDS.
+// minor, 64.25 KB) and per f = 0..4096 RU(1/f) with 4096 - f packed in (32 KB)
+// sit in LDS.
 // Exact quotient: floor(x/f) = trunc(fl64(x) * RU(1/f)) for x < 2^32, f <= 2^12
 // (the product stays below q+1 by more than the fp64 spacing there).
 // The group is coded backward (token n-1 first) and its words are written
@@ -710,7 +716,7 @@ __device__ __forceinline__ void slot_store(uint32_t v, uint32_t idx, __amdgpu_bu
       "s_nop 4\n\t"  // VALU-written SGPR operands of the store: see stream_load_async
       "buffer_store_short %0, %1, %2, %3 idxen"
       :
-      : "v"(v), "v"(idx), "s"(sw), "s"(soff));
+      : "v"(v), "v"(idx), "s"(sw), "s"(uni(soff)));
 }
 
 // On the lanes of m: store the low 16 bits of x as word idx after soff / 2,
@@ -737,28 +743,41 @@ __device__ __forceinline__ void renorm_out(uint32_t& x, uint64_t m, __amdgpu_buf
 //   S2: f of the entry, read RU(1/f)
 //   S3: escape payload, renormalisation word, state update
 struct EncTok {
-  uint32_t e;    // symbol entry f | b << 16 | escape << 31 (S1 read)
+  uint32_t e;    // symbol entry (16 f - 1) mod 2^16 | b << 16 (S1 read)
   uint32_t d16;  // low 16 bits: the wrapped delta, the escape payload
   bool esc;      // this lane codes an escape (wide delta, or robust tables)
   uint64_t me;   // lanes of the wavefront that need one
-  double r;      // RU(1/f)          } the frequency's constants (S2 read,
-  uint32_t g;    // 4096 - f         } one 16-byte LDS entry)
-  uint32_t t;    // f * 2^20 - 1: renormalise when x > t
+  double r;      // RU(1/f), 4096 - f in its low 16 bits (S2 read)
 };
 
-// Per-frequency constants of the encoder, one 16-byte LDS entry per f.
-// f = 0 (a symbol missing from plain tables, reported as CG_ERR_TABLE) gets
-// r = 0, g = 4096 and t = 2^32 - 1, which keep the state finite.
-struct alignas(16) FreqK {
-  double r;
-  uint32_t g, t;
-};
+// The encoder's constant for frequency f, one 8-byte LDS entry at 8 f:
+// RU(1/f), rounded up further to 36 significant bits, with 4096 - f in the
+// 16 low bits this frees. The stored value exceeds 1/f by a relative 2^-35
+// at most, below the 2^-32 / f that keeps trunc(x * r) = floor(x / f) for
+// every state x < f * 2^20 (the one below that the renormalisation leaves);
+// f = 4096 stays exact (2^-12). f = 0 holds 4096 in a zero value.
+__device__ __forceinline__ double enc_rcp(uint32_t f) {
+  if (f == 0) return __longlong_as_double(4096);
+  double r = 1.0 / (double)f;
+  if (__builtin_fma(r, (double)f, -1.0) < 0.0) r = __longlong_as_double(__double_as_longlong(r) + 1);
+  const uint64_t u = ((uint64_t)__double_as_longlong(r) + 0xFFFFu) & ~(uint64_t)0xFFFF;
+  return __longlong_as_double((long long)(u | (kM - f)));
+}
 
 // q_t - q_{t-1} wrapped to 16 bits and sign-extended, in one instruction
 // (the SDWA form sign-extends its 16-bit result)
 __device__ __forceinline__ int32_t sub_wrap16(int32_t a, int32_t b) {
   int32_t r;
   asm("v_sub_u32_sdwa %0, %1, %2 dst_sel:WORD_0 dst_unused:UNUSED_SEXT src0_sel:DWORD src1_sel:DWORD"
+      : "=v"(r)
+      : "v"(a), "v"(b));
+  return r;
+}
+
+// a + (b >> 16) in one instruction (the SDWA form reads b's high half)
+__device__ __forceinline__ uint32_t add_hi16(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1"
       : "=v"(r)
       : "v"(a), "v"(b));
   return r;
@@ -778,20 +797,19 @@ __device__ __forceinline__ void enc_s1(EncTok& k, uint16_t xprev, int32_t& qhi, 
   qhi = qlo;
 }
 
-// the escape decision comes from the entry: symbol 255 (a wide delta) and,
-// with robust tables, every symbol of frequency 0 carry the flag
-__device__ __forceinline__ void enc_s2(EncTok& k, const FreqK* fk) {
-  k.esc = (int32_t)k.e < 0;
+// The escape decision compares the entry with the lane's escape entry
+// (symbol 255, a wide delta and, with robust tables, every symbol of
+// frequency 0; kEncInvalid too). The reciprocal sits at byte 8 f, one past
+// half the entry's low half (16 f - 1); kEncInvalid's reaches f = 4096.
+__device__ __forceinline__ void enc_s2(EncTok& k, const uint8_t* rcp, uint32_t e_esc) {
+  k.esc = k.e >= e_esc;
   k.me = __ballot(k.esc);
-  const uint4 w = reinterpret_cast<const uint4*>(fk)[k.e & 0xFFFFu];
-  k.r = __hiloint2double((int)w.y, (int)w.x);
-  k.g = w.z;
-  k.t = w.w;
+  k.r = *reinterpret_cast<const double*>(rcp + ((k.e & 0xFFFFu) >> 1) + 1);
 }
 
-// Every entry of frequency 0 carries the escape flag (see k_norm), so an
-// escaping lane with f = 0 is the only way a symbol missing from the table
-// shows; the table is then invalid and the call reports CG_ERR_TABLE.
+// A symbol that plain tables cannot code (frequency 0, or an escape of
+// frequency 0) holds kEncInvalid, which counts as an escape, so the escape
+// branch is the only place it shows; the call then reports CG_ERR_TABLE.
 // (reported from inside the branch: a flag carried to the end of the group
 // would be updated by a select on every token)
 __device__ __forceinline__ void enc_s3(const EncTok& k, uint32_t& x, uint32_t& P, __amdgpu_buffer_rsrc_t sr,
@@ -799,17 +817,19 @@ __device__ __forceinline__ void enc_s3(const EncTok& k, uint32_t& x, uint32_t& P
   if (k.me) {
     P -= (uint32_t)__popcll(k.me);
     if (k.esc) slot_store(k.d16, mbcnt_base(k.me, 0), sr, 2u * P);
-    if (__builtin_expect(__ballot(k.esc && (k.e & 0xFFFFu) == 0) != 0, 0) && lane == 0)
+    if (__builtin_expect(__ballot(k.esc && k.e == kEncInvalid) != 0, 0) && lane == 0)
       set_status(status, CG_ERR_TABLE);
   }
-  // renormalise when x >= f * 2^20 (never for f = 4096: x < 2^32)
-  const uint64_t mr = __ballot(x > k.t);
+  // renormalise when x >= f * 2^20, i.e. x >> 16 >= 16 f (never for
+  // f = 4096, whose entry's low half is 65535)
+  const uint64_t mr = __ballot((x >> 16) > (k.e & 0xFFFFu));
   P -= (uint32_t)__popcll(mr);
   renorm_out(x, mr, sr, mbcnt_base(mr, 0), 2u * P);
   // x <- floor(x/f)*4096 + x mod f + b = x + floor(x/f)*(4096-f) + b; the
-  // quotient is < 2^20 and 4096 - f < 2^12, so a 24-bit multiply is exact.
+  // quotient is < 2^20 and 4096 - f <= 2^12, so a 24-bit multiply is exact.
   const uint32_t qd = (uint32_t)((double)x * k.r);
-  x = __umul24(qd, k.g) + x + ((k.e >> 16) & 0x7FFFu);
+  const uint32_t g = (uint32_t)__double_as_longlong(k.r) & 0xFFFFu;
+  x = add_hi16(__umul24(qd, g) + x, k.e);
 }
 
 // Encodes tokens n-1 .. 1 of a group (backward), then the head. xr covers the
@@ -818,12 +838,13 @@ __device__ __forceinline__ void enc_s3(const EncTok& k, uint32_t& x, uint32_t& P
 template <int QM, bool BF>
 __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, uint32_t row_bytes,
                                              const Quot qc, const uint32_t* ftab,
-                                             const FreqK* fk, __amdgpu_buffer_rsrc_t sr,
+                                             const uint8_t* fk, __amdgpu_buffer_rsrc_t sr,
                                              uint32_t cap, int lane, uint32_t& words,
                                              uint32_t& start, int32_t* status, int* left, int wave,
                                              int left_after) {
   const uint32_t lane2 = 2u * lane;
   const uint32_t* row0 = ftab + 128 * 64 + lane;
+  const uint32_t e_esc = ftab[lane];  // row 0: the escape's entry
   uint32_t P = cap;
   uint32_t x = kL;
   auto row = [&](int r) { return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(xr, lane2, (uint32_t)r * row_bytes, 0); };
@@ -834,7 +855,7 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
     // S2, token n-2 through S1.
     EncTok a, b, c;
     enc_s1<QM, BF>(a, row(n - 2), qhi, qc, row0);
-    enc_s2(a, fk);
+    enc_s2(a, fk, e_esc);
     enc_s1<QM, BF>(b, row(n - 3), qhi, qc, row0);
     // tokens i, i-1, ... enter S1 with x of rows i-1, i-2, ...; the rows of
     // the next batch are loaded while the current one is encoded. Offsets
@@ -869,7 +890,7 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
     __builtin_amdgcn_s_waitcnt(0x0F70);  // as in hist_range
     auto advance = [&](uint16_t xprev) {
       enc_s1<QM, BF>(c, xprev, qhi, qc, row0);
-      enc_s2(b, fk);
+      enc_s2(b, fk, e_esc);
       enc_s3(a, x, P, sr, status, lane);
       a = b;
       b = c;
@@ -907,13 +928,13 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
     for (int k = 0; k < kEncBatch; ++k)  // the last i < 16 tokens
       if (k < i) advance((uint16_t)xa[k]);
     // epilogue: the last two tokens leave the pipeline
-    enc_s2(b, fk);
+    enc_s2(b, fk, e_esc);
     enc_s3(a, x, P, sr, status, lane);
     enc_s3(b, x, P, sr, status, lane);
   } else if (n == 2) {
     EncTok a;
     enc_s1<QM, BF>(a, row(0), qhi, qc, row0);
-    enc_s2(a, fk);
+    enc_s2(a, fk, e_esc);
     enc_s3(a, x, P, sr, status, lane);
   }
   P -= 64;
@@ -954,16 +975,16 @@ __device__ __forceinline__ int layers_in_group(const uint8_t* blob, int G, int L
 }
 
 // LDS of the encoder, laid out by hand so both tables sit at small fixed
-// offsets: the per-frequency constants first (address f * 16), then the
+// offsets: the per-frequency constants first (address f * 8), then the
 // symbol table.
-constexpr int kEncRcpBytes = 16 * (kM + 1);
+constexpr int kEncRcpBytes = 8 * (kM + 1);
 constexpr int kEncFtabOff = (kEncRcpBytes + 255) / 256 * 256;
 
 template <bool BF>
 __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
   __shared__ __align__(16) uint8_t enc_lds[kEncFtabOff + 4 * kEncDwords * 64];
   __shared__ int left[kWaves];
-  FreqK* fk = reinterpret_cast<FreqK*>(enc_lds);
+  double* fk = reinterpret_cast<double*>(enc_lds);
   uint32_t* ftab = reinterpret_cast<uint32_t*>(enc_lds + kEncFtabOff);
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const Shape s = a.s;
@@ -994,12 +1015,7 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
   const uint4* esrc = reinterpret_cast<const uint4*>(
       reinterpret_cast<const uint32_t*>(a.blob + tb_enc_offset(s.L, s.H, s.D, G)) + set * (kEncDwords * 64));
   for (int u = tid; u < kEncDwords * 64 / 4; u += kEncThreads) reinterpret_cast<uint4*>(ftab)[u] = esrc[u];
-  for (int f = tid + 1; f <= (int)kM; f += kEncThreads) {
-    double r = 1.0 / (double)f;
-    if (__builtin_fma(r, (double)f, -1.0) < 0.0) r = __longlong_as_double(__double_as_longlong(r) + 1);
-    fk[f] = FreqK{r, kM - (uint32_t)f, (uint32_t)(((uint64_t)f << 20) - 1)};
-  }
-  if (tid == 0) fk[0] = FreqK{0.0, kM, 0xFFFFFFFFu};
+  for (int f = tid; f <= (int)kM; f += kEncThreads) fk[f] = enc_rcp((uint32_t)f);
   if (tid < kWaves) left[tid] = 0x7FFFFFFF;
   __syncthreads();
 
@@ -1028,7 +1044,7 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(xb, (uint32_t)n * row_bytes);
     uint32_t words, start;
 #define CG_ENC(QM) \
-  encode_group<QM, BF>(xr, (int)n, row_bytes, qc, ftab, fk, sr, cap, lane, words, start, a.status, \
+  encode_group<QM, BF>(xr, (int)n, row_bytes, qc, ftab, enc_lds, sr, cap, lane, words, start, a.status, \
                left, wave, my_left)
     if (qm == kQuotMul) CG_ENC(kQuotMul);
     else if (qm == kQuotTwo) CG_ENC(kQuotTwo);

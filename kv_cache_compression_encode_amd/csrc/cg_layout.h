@@ -38,11 +38,15 @@ constexpr int kMaxLayers = 1024;
 // above and rankx lie in the first 64 KB so one ds_read2st64 fetches both.
 constexpr int kDecDwords = 512;            // per channel
 constexpr int kDecBm = 0, kDecRb = 128 * 64, kDecInfo = 256 * 64;  // dword offsets in a set
-// Encoder set: [257 rows][64] of f | b << 16 | escape << 31, indexed by the
-// token delta d clamped to [-128, 128], plus 128: row r = 1..255 holds
+// Encoder set: [257 rows][64] of (16 f - 1) mod 2^16 | b << 16, indexed by
+// the token delta d clamped to [-128, 128], plus 128: row r = 1..255 holds
 // symbol r - 1 (d = r - 128), rows 0 and 256 the escape symbol's entry (d
-// below -127 or above 127). 64.25 KB.
+// below -127 or above 127). A symbol that plain tables cannot code (f = 0,
+// or an escape of f = 0) holds kEncInvalid. The escape symbol is the last
+// in cumulative order, so its b, and hence its entry, exceeds every other
+// coded symbol's: entry >= the escape's entry means "escape". 64.25 KB.
 constexpr int kEncDwords = 257;            // per channel
+constexpr uint32_t kEncInvalid = 0xFFFFFFFFu;
 // Decoder ring per chain: 256 16-bit words refilled 128 at a time (one dword
 // per lane), plus a 64-word mirror of words 0..63 so a read at
 // (p mod 256) + k, k < 64, needs no wrap.
