@@ -740,7 +740,7 @@ __device__ __forceinline__ void renorm_out(uint32_t& x, uint64_t m, __amdgpu_buf
 // after the previous one so that its LDS read lands behind a token of other
 // work instead of being waited for at once:
 //   S1: quantize x_{t-1}, symbol of q_t - q_{t-1}, read the symbol's entry
-//   S2: f of the entry, read RU(1/f)
+//   S2: escape test on the entry, read f's reciprocal
 //   S3: escape payload, renormalisation word, state update
 struct EncTok {
   uint32_t e;    // symbol entry (16 f - 1) mod 2^16 | b << 16 (S1 read)
@@ -838,7 +838,7 @@ __device__ __forceinline__ void enc_s3(const EncTok& k, uint32_t& x, uint32_t& P
 template <int QM, bool BF>
 __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, uint32_t row_bytes,
                                              const Quot qc, const uint32_t* ftab,
-                                             const uint8_t* fk, __amdgpu_buffer_rsrc_t sr,
+                                             const uint8_t* rcp, __amdgpu_buffer_rsrc_t sr,
                                              uint32_t cap, int lane, uint32_t& words,
                                              uint32_t& start, int32_t* status, int* left, int wave,
                                              int left_after) {
@@ -855,7 +855,7 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
     // S2, token n-2 through S1.
     EncTok a, b, c;
     enc_s1<QM, BF>(a, row(n - 2), qhi, qc, row0);
-    enc_s2(a, fk, e_esc);
+    enc_s2(a, rcp, e_esc);
     enc_s1<QM, BF>(b, row(n - 3), qhi, qc, row0);
     // tokens i, i-1, ... enter S1 with x of rows i-1, i-2, ...; the rows of
     // the next batch are loaded while the current one is encoded. Offsets
@@ -890,7 +890,7 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
     __builtin_amdgcn_s_waitcnt(0x0F70);  // as in hist_range
     auto advance = [&](uint16_t xprev) {
       enc_s1<QM, BF>(c, xprev, qhi, qc, row0);
-      enc_s2(b, fk, e_esc);
+      enc_s2(b, rcp, e_esc);
       enc_s3(a, x, P, sr, status, lane);
       a = b;
       b = c;
@@ -928,13 +928,13 @@ __device__ __forceinline__ void encode_group(__amdgpu_buffer_rsrc_t xr, int n, u
     for (int k = 0; k < kEncBatch; ++k)  // the last i < 16 tokens
       if (k < i) advance((uint16_t)xa[k]);
     // epilogue: the last two tokens leave the pipeline
-    enc_s2(b, fk, e_esc);
+    enc_s2(b, rcp, e_esc);
     enc_s3(a, x, P, sr, status, lane);
     enc_s3(b, x, P, sr, status, lane);
   } else if (n == 2) {
     EncTok a;
     enc_s1<QM, BF>(a, row(0), qhi, qc, row0);
-    enc_s2(a, fk, e_esc);
+    enc_s2(a, rcp, e_esc);
     enc_s3(a, x, P, sr, status, lane);
   }
   P -= 64;
@@ -984,7 +984,7 @@ template <bool BF>
 __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
   __shared__ __align__(16) uint8_t enc_lds[kEncFtabOff + 4 * kEncDwords * 64];
   __shared__ int left[kWaves];
-  double* fk = reinterpret_cast<double*>(enc_lds);
+  double* rcp_tab = reinterpret_cast<double*>(enc_lds);
   uint32_t* ftab = reinterpret_cast<uint32_t*>(enc_lds + kEncFtabOff);
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const Shape s = a.s;
@@ -1015,7 +1015,7 @@ __global__ void __launch_bounds__(kEncThreads) k_encode(EncodeArgs a) {
   const uint4* esrc = reinterpret_cast<const uint4*>(
       reinterpret_cast<const uint32_t*>(a.blob + tb_enc_offset(s.L, s.H, s.D, G)) + set * (kEncDwords * 64));
   for (int u = tid; u < kEncDwords * 64 / 4; u += kEncThreads) reinterpret_cast<uint4*>(ftab)[u] = esrc[u];
-  for (int f = tid; f <= (int)kM; f += kEncThreads) fk[f] = enc_rcp((uint32_t)f);
+  for (int f = tid; f <= (int)kM; f += kEncThreads) rcp_tab[f] = enc_rcp((uint32_t)f);
   if (tid < kWaves) left[tid] = 0x7FFFFFFF;
   __syncthreads();
 
