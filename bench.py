@@ -359,8 +359,11 @@ def main():
                     "decode_share_of_round_trip": round(float(t_dec) / (wall / args.steps * 1e3), 4)},
         "roofline": roof(dom),
         "roofline_decode": roof("k_decode"),
+        "roofline_encode": roof("k_encode"),
+        "roofline_build": roof("k_hist"),
         "roofline_alu": roof_alu(dom),
         "roofline_alu_decode": roof_alu("k_decode"),
+        "roofline_alu_encode": roof_alu("k_encode"),
         "kernel_ms": {"k_hist": round(kms["build"], 4), "k_encode": round(kms["encode"], 4),
                       "k_decode": round(kms["decode"], 4)},
         "copy_GBps": round(copy_gbps, 1) if copy_gbps else None,
