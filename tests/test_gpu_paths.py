@@ -131,6 +131,42 @@ def test_decode_corrupt_record_status(multi):
     assert cd.read_status() == C.CG_ERR_CORRUPT
 
 
+def test_decode_random_damage_matches_oracle(multi):
+    """Seeded single-bit damage anywhere in a record past its header (group
+    directory, word streams, padding): the decoder ends normally with the
+    oracle's status, and where both accept the record (a changed head word
+    or padding), with the oracle's values."""
+    cfg, X, cd, gl, tabs, outs, oshp, oracle = multi
+    out, offs = outs[0]
+    o = offs.cpu().numpy()
+    rec = out[int(o[1]):int(o[2])].clone()
+    n = rec.numel()
+    ds = O.record_data_start(oshp)
+    blob = oracle[0][0]
+    rng = np.random.default_rng(11)
+    positions = [int(p) for p in rng.integers(64, ds, size=6)] + [int(p) for p in rng.integers(ds, n, size=18)]
+    seen = set()
+    for pos in positions:
+        bit = int(rng.integers(8))
+        bad = rec.clone()
+        bad[pos] ^= 1 << bit
+        print("damage byte", pos, "bit", bit, flush=True)
+        refs, nr = cd.make_refs([(bad, torch.tensor([0, n]), [0], 0)])
+        y = torch.zeros((cfg.layers, 2, cfg.kv_heads, cfg.tokens, cfg.head_dim), dtype=torch.float16,
+                        device="cuda")
+        cd.decode([gl[0]], [tabs[0]], refs, nr, y=y)
+        st = cd.read_status()
+        Y = np.zeros(y.shape, dtype=np.uint16)
+        ost = O.decode_chunk(oshp, blob, bad.cpu().numpy(), Y)
+        assert (st == C.CG_ERR_CORRUPT) == (ost == O.ERR_CORRUPT) and (st == 0) == (ost == 0), (pos, bit, st, ost)
+        seen.add(st)
+        if st == 0:
+            c0 = cfg.chunk_tokens
+            got = y.cpu().view(torch.int16).numpy().view(np.uint16)[:, :, :, c0:2 * c0]
+            assert np.array_equal(got, Y[:, :, :, c0:2 * c0]), (pos, bit)
+    assert C.CG_ERR_CORRUPT in seen
+
+
 def test_table_index_and_level_checks(multi):
     cfg, X, cd, gl, tabs, outs, oshp, oracle = multi
     out, offs = outs[0]
