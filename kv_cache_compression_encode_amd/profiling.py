@@ -200,6 +200,8 @@ def main():
     q.add_argument("--command", required=True, help="the command, ';'-separated lines")
     q.add_argument("--json", required=True)
     q.add_argument("--md", required=True)
+    q.add_argument("--skip", type=int, default=2, help="warm-up launches of the kernel-trace run")
+    q.add_argument("--count", type=int, default=5, help="timed launches of the kernel-trace run")
     a = ap.parse_args()
     if a.cmd == "stall":
         res = stall(a.a, a.b)
@@ -225,7 +227,7 @@ def main():
         print("wrote", a.md)
         return
     if a.cmd == "sq":
-        res = sq(a.sq, a.trace)
+        res = sq(a.sq, a.trace, skip=a.skip, count=a.count)
         doc = {}
         if os.path.exists(a.json):
             with open(a.json) as f:
@@ -240,8 +242,8 @@ def main():
         with open(a.md, "w") as f:
             f.write("# SQ counters per launch, %s workload (rocprofv3)\n\n" % a.config)
             f.write("Kernel sources: hash `%s`. VALU peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = %.2f T "
-                    "lane-ops/s (int32 / non-packed fp32). Counters: the first dispatch of each kernel (the one timed step). Durations: the kernel-trace run's timed launches (after 2 warm-up steps, the 5 timed steps).\n\n"
-                    % (source_hash(), VALU_PEAK_OPS / 1e12))
+                    "lane-ops/s (int32 / non-packed fp32). Counters: the first dispatch of each kernel (the one timed step). Durations: the kernel-trace run's timed launches (after %d warm-up steps, the %d timed steps).\n\n"
+                    % (source_hash(), VALU_PEAK_OPS / 1e12, a.skip, a.count))
             f.write("Commands (repository root):\n\n```\n%s\n```\n\n" % a.command.replace(";", "\n"))
             f.write("| kernel | avg us | waves | VALU insts | SALU insts | LDS insts | VALU lane-ops/s | of VALU "
                     "peak | LDS bank conflicts | wait-any / wave-busy |\n|---|---|---|---|---|---|---|---|---|---|\n")
@@ -277,8 +279,8 @@ def main():
                 f.write("\nTimed launches only (each codec kernel's first %d launches, the warm-up steps, left "
                         "out%s), from the per-dispatch trace%s:\n\n" % (
                             a.skip, ", and only the next %d, the timed steps" % steps if steps else "",
-                            ", beside the HIP-event averages bench.py printed in the same run"
-                            if bench else ""))
+                            ", beside the HIP-event averages bench.py printed in the same run (from "
+                            "its steps with timing events, which follow the timed ones)" if bench else ""))
                 f.write("| kernel | timed launches | trace average us | bench.py events us | trace / events |\n"
                         "|---|---|---|---|---|\n")
                 for k, (nl, us) in sorted(ta.items()):
