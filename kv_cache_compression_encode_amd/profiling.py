@@ -279,8 +279,8 @@ def main():
                 f.write("\nTimed launches only (each codec kernel's first %d launches, the warm-up steps, left "
                         "out%s), from the per-dispatch trace%s:\n\n" % (
                             a.skip, ", and only the next %d, the timed steps" % steps if steps else "",
-                            ", beside the HIP-event averages bench.py printed in the same run (from "
-                            "its steps with timing events, which follow the timed ones)" if bench else ""))
+                            ", beside the HIP-event averages bench.py printed in the same run"
+                            if bench else ""))
                 f.write("| kernel | timed launches | trace average us | bench.py events us | trace / events |\n"
                         "|---|---|---|---|---|\n")
                 for k, (nl, us) in sorted(ta.items()):
