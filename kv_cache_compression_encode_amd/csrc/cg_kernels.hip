@@ -721,12 +721,15 @@ __device__ __forceinline__ void slot_store(uint32_t v, uint32_t idx, __amdgpu_bu
 
 // On the lanes of m: store the low 16 bits of x as word idx after soff / 2,
 // then x >>= 16. One masked region with a single VALU shift; the compiler's
-// version computes the shift into a temporary and copies it back.
+// version computes the shift into a temporary and copies it back. No wait
+// states before the store: its scalar operands (the slot descriptor, the
+// word offset) come from scalar instructions, and tests/asm_hazards.py checks
+// in the compiled code that no VALU write of them falls within the five wait
+// states a vector-memory read of a VALU-written SGPR needs.
 __device__ __forceinline__ void renorm_out(uint32_t& x, uint64_t m, __amdgpu_buffer_rsrc_t sw,
                                            uint32_t idx, uint32_t soff) {
   uint64_t saved;
   asm volatile(
-      "s_nop 4\n\t"  // VALU-written SGPR operands of the store: see stream_load_async
       "s_and_saveexec_b64 %1, %2\n\t"
       "buffer_store_short %0, %3, %4, %5 idxen\n\t"
       "v_lshrrev_b32 %0, 16, %0\n\t"
